@@ -1,0 +1,195 @@
+/*
+ * lowbit.h -- C ABI of the group-scaled 1-bit / ternary y = W.x library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section; the method is described only in
+ * prose on these pages, and no code or API is given there):
+ *   [P1] 7minutos.es, "Un tutorial de codificacion para ejecutar PrismML Bonsai
+ *        1-bit LLM en CUDA con GGUF", section 7 "Q1_0_g128 Cuantizacion"
+ *        (the representation box and the Python demonstration of the rule).
+ *   [P2] 7minutos.es, "PrismML lanza Bonsai 27B: compilaciones ternarias y de
+ *        1 bit de Qwen3.6-27B", sections "Como funciona la compresion" and
+ *        "Rendimiento y decodificacion especulativa DSpark".
+ *   [P3] kerneldigest.dev, "Bonsai 2 27B y la densidad de inteligencia",
+ *        section "Arquitectura del Sistema".
+ *   [P4] es.news.hada.io topic 31450, "Bonsai 27B: un modelo de clase 27B que
+ *        corre en un telefono", section "Configuracion multimodal y de bajo bit
+ *        de extremo a extremo" and the reader comments.
+ *
+ * ---------------------------------------------------------------------------
+ * THE TWO WEIGHT CODES
+ *
+ *   Q1_0_g128 [P1 s.7]: every weight is one bit; bit 0 stands for -s and bit 1
+ *     for +s, where s is an FP16 scale shared by 128 consecutive weights.
+ *     Quantisation from FP16: s = max |w| over the 128 weights of the group and
+ *     bit = 1 when w >= 0, else 0.  1 + 16/128 = 1.125 bits per weight.
+ *   Ternary g128 [P2 "Como funciona la compresion", P3]: w = s * t with
+ *     t in {-1, 0, +1} and one FP16 scale s per 128 consecutive weights.  The
+ *     pages count log2(3) bits per weight; this library stores two bits per
+ *     weight ("four values of four states" per byte, [P4 comments]):
+ *     2 + 16/128 = 2.125 bits per weight.
+ *
+ * The group of 128 runs along K, the reduction axis: W is logical [N][K] and
+ * group g of row n holds k in [128 g, 128 g + 128).  K must be a multiple of
+ * 128.  The pages do not fix a bit order or byte layout; this library defines
+ * its own, below.  Both codes keep the pages' per-group byte count:
+ * 16 code bytes + 2 scale bytes = 18 B per Q1 group, 32 + 2 = 34 B per
+ * ternary group (stored as two separate planes, codes and scales).
+ *
+ * ---------------------------------------------------------------------------
+ * BYTE LAYOUT (version 1)
+ *
+ *   Np      = N rounded up to a multiple of 16 (rows are stored in tiles of 16)
+ *   tile    = n / 16, r = n % 16   (row tile and row within the tile)
+ *   c       = k / 8                (8-weight chunk), j = k % 8 (bit in byte)
+ *   G       = K / 128, g = k / 128 (group)
+ *
+ *   Q1 codes:  Np*K/8 bytes.  The bit of weight (n,k) is bit j (value 1<<j) of
+ *              byte  (tile*(K/8) + c)*16 + r.
+ *              A 16-byte "cell" holds one 8-weight chunk of 16 rows.
+ *   T2 codes:  Np*K/4 bytes, 32-byte cells.  For weight (n,k):
+ *                pos bit = bit j of byte (tile*(K/8) + c)*32 + r
+ *                neg bit = bit j of byte (tile*(K/8) + c)*32 + 16 + r
+ *              t = pos - neg  (so pos=neg=1 decodes as 0; packers never
+ *              write that pattern).
+ *   scales:    Np*G FP16 values (2 bytes each).  The scale of (n, g) is
+ *              element (tile*G + g)*16 + r.
+ *   Pad rows (N <= n < Np) hold zero codes and zero scales; they are written
+ *   by the packers and never read into an output.
+ *
+ * ---------------------------------------------------------------------------
+ * CONVENTIONS FOR EVERY ENTRY POINT
+ *
+ *   - Pointers are HIP device pointers unless stated otherwise; the caller
+ *     allocates and frees every buffer.  The library never allocates,
+ *     frees or synchronises, and keeps no state between calls.
+ *   - FP16 and BF16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Every call validates its arguments on the host, then enqueues its
+ *     kernels on `stream` and returns without waiting.  On a validation
+ *     error nothing is launched and the return value says why.  A failed
+ *     launch returns LOWBIT_ERR_HIP.  Faults during execution surface at the
+ *     caller's next synchronisation.
+ *   - Shapes: n >= 1, k >= 128 and k % 128 == 0, n*k < 2^40; GEMV batch
+ *     1 <= b <= 8; GEMM m >= 1.
+ *   - Alignment: codes, scales, x, y, w and workspace pointers must be 16-byte
+ *     aligned (torch's allocator gives 256).
+ *   - Buffers of one call must not overlap, except that read-only inputs may
+ *     alias each other.  Calls on different streams that share an output or
+ *     a workspace race.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOWBIT_FMT_Q1_G128 = 1, /* 1-bit codes, bit 1 -> +s, bit 0 -> -s  [P1 s.7] */
+  LOWBIT_FMT_T2_G128 = 2  /* ternary codes t = pos - neg, w = s*t   [P2, P3]   */
+} lowbit_fmt;
+
+typedef enum {
+  LOWBIT_OK = 0,
+  LOWBIT_ERR_ARG = 1,         /* null pointer, unknown format, bad batch/m   */
+  LOWBIT_ERR_SHAPE = 2,       /* n < 1, k % 128 != 0, size too large          */
+  LOWBIT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned             */
+  LOWBIT_ERR_UNSUPPORTED = 4, /* valid request this build does not implement */
+  LOWBIT_ERR_HIP = 5,         /* a HIP call or kernel launch failed           */
+  LOWBIT_ERR_WORKSPACE = 6    /* workspace missing or smaller than required  */
+} lowbit_status;
+
+/* Library ABI version (this header describes version 1). */
+int lowbit_version(void);
+
+/* Human-readable name of a status code; never NULL. */
+const char* lowbit_status_str(int status);
+
+/* Bytes of the code plane / scale plane for an n x k matrix in `fmt`.
+ * Q1: Np*k/8, T2: Np*k/4, scales: Np*(k/128)*2, with Np = n rounded up to 16.
+ * Returns 0 for an invalid format or shape.  Host-only; touches no GPU. */
+size_t lowbit_codes_bytes(int fmt, int64_t n, int64_t k);
+size_t lowbit_scales_bytes(int fmt, int64_t n, int64_t k);
+
+/* Q1 quantise + pack  [P1 s.7: scale = max|w| per 128, bit = 1 iff w >= 0].
+ *   w_fp16 : [n][k] row-major FP16 weights (device, read-only).
+ *   codes  : lowbit_codes_bytes(Q1, n, k) bytes (device, written).
+ *   scales : lowbit_scales_bytes(Q1, n, k) bytes (device, written).
+ * Exact integer rules on the FP16 bit pattern h (mag = h & 0x7FFF):
+ *   s = max over the group of mag (as an FP16 pattern with sign 0): this is
+ *       max|w| for finite/infinite input; a group holding a NaN gets the NaN
+ *       pattern of largest magnitude bits.
+ *   bit = 1 iff the IEEE comparison w >= 0 holds: +0 and -0 give 1, every NaN
+ *       gives 0.  Subnormals are handled exactly (no flush to zero). */
+int lowbit_quantize_q1(const uint16_t* w_fp16, int64_t n, int64_t k,
+                       void* codes, uint16_t* scales, hipStream_t stream);
+
+/* Ternary pack  [P2 "Como funciona la compresion": w = s_g * t_i].
+ *   t      : [n][k] row-major int8 (device, read-only); the stored code is
+ *            sign(t), so values outside {-1,0,1} are clamped by their sign.
+ *   s_fp16 : [n][k/128] row-major FP16 group scales (device, read-only),
+ *            copied bit for bit.
+ *   codes, scales : as for lowbit_quantize_q1, in the T2 layout. */
+int lowbit_pack_t2(const int8_t* t, const uint16_t* s_fp16, int64_t n,
+                   int64_t k, void* codes, uint16_t* scales,
+                   hipStream_t stream);
+
+/* Generic pack entry: Q1 -> lowbit_quantize_q1(src as FP16, src_scales must be
+ * NULL); T2 -> lowbit_pack_t2(src as int8, src_scales as FP16). */
+int lowbit_pack(int fmt, const void* src, const uint16_t* src_scales,
+                int64_t n, int64_t k, void* codes, uint16_t* scales,
+                hipStream_t stream);
+
+/* Unpack / dequantise to dense FP16 [P1 s.7 dequantisation rule, P2].
+ *   w_fp16 : [n][k] row-major FP16 output (device, written).
+ * Q1: bit 1 -> s, bit 0 -> s with its sign bit flipped (-s).
+ * T2: t = +1 -> s, t = -1 -> s with its sign bit flipped, t = 0 -> +0.0.
+ * Every output value is exact (a copy of s or of its negation). */
+int lowbit_unpack(int fmt, const void* codes, const uint16_t* scales,
+                  int64_t n, int64_t k, uint16_t* w_fp16, hipStream_t stream);
+
+/* Workspace bytes lowbit_gemv needs for (fmt, n, k, b); 0 on a bad shape. */
+size_t lowbit_gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b);
+
+/* Decode GEMV  [P2 "Rendimiento ...": decode streams every low-bit matrix once
+ * per token; P4: embeddings, attention, MLP and LM head are all low-bit].
+ *   y[i][n] = sum_g s[n][g] * sum_{k in g} t[n][k] * x[i][k],  0 <= i < b
+ *   x_fp16    : [b][k] row-major FP16 activations (device, read-only)
+ *   y_f32     : [b][n] row-major FP32 output (device, written)
+ *   workspace : at least lowbit_gemv_workspace_bytes(fmt, n, k, b) bytes of
+ *               device scratch, contents ignored on entry and clobbered.
+ * Accumulates in FP32; the summation order is not specified and, because
+ * K-slices are combined with atomic adds, may differ from run to run in the
+ * last bits. */
+int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales,
+                int64_t n, int64_t k, const uint16_t* x_fp16, int64_t b,
+                float* y_f32, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Prefill GEMM  [P2 "Rendimiento ...": prefill is compute-bound].
+ *   Y[i][n] = RNE_bf16( sum_g s[n][g] * sum_{k in g} X[i][k] * t[n][k] )
+ *   x_bf16 : [m][k] row-major BF16 (device, read-only)
+ *   y_bf16 : [m][n] row-major BF16 (device, written)
+ * Codes are expanded to exact BF16 {-1,0,+1}, contracted on matrix cores in
+ * FP32, and each 128-wide group's partial is multiplied by its scale in FP32
+ * before accumulation; the single rounding to BF16 happens at the store. */
+int lowbit_gemm(int fmt, const void* codes, const uint16_t* scales,
+                int64_t n, int64_t k, const uint16_t* x_bf16, int64_t m,
+                uint16_t* y_bf16, hipStream_t stream);
+
+/* Same contraction as lowbit_gemm with the FP32 sum stored unrounded:
+ *   y_f32 : [m][n] row-major FP32 (device, written). */
+int lowbit_gemm_f32(int fmt, const void* codes, const uint16_t* scales,
+                    int64_t n, int64_t k, const uint16_t* x_bf16, int64_t m,
+                    float* y_f32, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */
