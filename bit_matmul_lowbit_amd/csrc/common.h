@@ -1,0 +1,38 @@
+// Internal declarations shared by the HIP sources of liblowbit.so.
+// Layout constants follow include/lowbit.h (version 1): 16-row tiles, 8-weight
+// chunks (one byte per row per chunk), 128-weight groups along K.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+constexpr int kTileRows = 16;   // rows per tile
+constexpr int kChunk = 8;       // weights per code byte
+constexpr int kGroup = 128;     // weights per scale
+constexpr int kChunksPerGroup = kGroup / kChunk;
+
+// cell bytes: 16 rows x 1 byte (Q1) or 16 rows x (pos byte, neg byte) (T2)
+template <int FMT> struct Fmt;
+template <> struct Fmt<1> { static constexpr int cell_bytes = 16; };
+template <> struct Fmt<2> { static constexpr int cell_bytes = 32; };
+
+// Kernel launchers (host side, defined in the .hip files).  All return a
+// hipError_t from the launch; shapes were validated by the caller.
+hipError_t launch_quantize_q1(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                              uint16_t* scales, hipStream_t st);
+hipError_t launch_pack_t2(const int8_t* t, const uint16_t* s, int64_t n, int64_t k,
+                          uint8_t* codes, uint16_t* scales, hipStream_t st);
+hipError_t launch_unpack(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                         int64_t k, uint16_t* w, hipStream_t st);
+
+size_t gemv_workspace_bytes(int64_t k, int64_t b);
+hipError_t launch_gemv(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                       int64_t k, const uint16_t* x, int64_t b, float* y, void* ws,
+                       hipStream_t st);
+
+hipError_t launch_gemm(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                       int64_t k, const uint16_t* x, int64_t m, void* y, bool out_f32,
+                       hipStream_t st);
+
+}  // namespace lowbit

@@ -1,0 +1,140 @@
+// C ABI of liblowbit.so: argument validation on the host, then kernel
+// dispatch.  The contract of every entry point is in include/lowbit.h.
+#include "../../include/lowbit.h"
+
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxK = int64_t(1) << 22;
+
+bool fmt_ok(int fmt) { return fmt == LOWBIT_FMT_Q1_G128 || fmt == LOWBIT_FMT_T2_G128; }
+
+bool shape_ok(int64_t n, int64_t k) {
+  if (n < 1 || k < 128 || k % 128 != 0 || k > kMaxK) return false;
+  if (n > kMaxElems / k) return false;
+  return ((n + 15) / 16) < (int64_t(1) << 31);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t padded(int64_t n) { return (n + 15) / 16 * 16; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int lowbit_version(void) { return 1; }
+
+const char* lowbit_status_str(int status) {
+  switch (status) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_ERR_ARG: return "invalid argument (null pointer, format, batch or m)";
+    case LOWBIT_ERR_SHAPE: return "invalid shape (n >= 1, k >= 128, k % 128 == 0, size limits)";
+    case LOWBIT_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LOWBIT_ERR_UNSUPPORTED: return "unsupported request";
+    case LOWBIT_ERR_HIP: return "HIP launch failed";
+    case LOWBIT_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t lowbit_codes_bytes(int fmt, int64_t n, int64_t k) {
+  if (!fmt_ok(fmt) || !shape_ok(n, k)) return 0;
+  return (size_t)(padded(n) * k / (fmt == LOWBIT_FMT_Q1_G128 ? 8 : 4));
+}
+
+size_t lowbit_scales_bytes(int fmt, int64_t n, int64_t k) {
+  if (!fmt_ok(fmt) || !shape_ok(n, k)) return 0;
+  return (size_t)(padded(n) * (k / 128) * 2);
+}
+
+int lowbit_quantize_q1(const uint16_t* w_fp16, int64_t n, int64_t k, void* codes,
+                       uint16_t* scales, hipStream_t stream) {
+  if (!w_fp16 || !codes || !scales) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(w_fp16) || !aligned16(codes) || !aligned16(scales)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_quantize_q1(w_fp16, n, k, static_cast<uint8_t*>(codes),
+                                               scales, stream));
+}
+
+int lowbit_pack_t2(const int8_t* t, const uint16_t* s_fp16, int64_t n, int64_t k, void* codes,
+                   uint16_t* scales, hipStream_t stream) {
+  if (!t || !s_fp16 || !codes || !scales) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  // t rows are read 8 bytes at a time; s is read element-wise
+  if (!aligned16(t) || !aligned16(codes) || !aligned16(scales) ||
+      (reinterpret_cast<uintptr_t>(s_fp16) & 1u))
+    return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_pack_t2(t, s_fp16, n, k, static_cast<uint8_t*>(codes), scales,
+                                           stream));
+}
+
+int lowbit_pack(int fmt, const void* src, const uint16_t* src_scales, int64_t n, int64_t k,
+                void* codes, uint16_t* scales, hipStream_t stream) {
+  if (fmt == LOWBIT_FMT_Q1_G128) {
+    if (src_scales) return LOWBIT_ERR_ARG;
+    return lowbit_quantize_q1(static_cast<const uint16_t*>(src), n, k, codes, scales, stream);
+  }
+  if (fmt == LOWBIT_FMT_T2_G128)
+    return lowbit_pack_t2(static_cast<const int8_t*>(src), src_scales, n, k, codes, scales,
+                          stream);
+  return LOWBIT_ERR_ARG;
+}
+
+int lowbit_unpack(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                  uint16_t* w_fp16, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !w_fp16) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_fp16)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_unpack(fmt, static_cast<const uint8_t*>(codes), scales, n, k,
+                                          w_fp16, stream));
+}
+
+size_t lowbit_gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b) {
+  if (!fmt_ok(fmt) || !shape_ok(n, k) || b < 1 || b > 8) return 0;
+  return lowbit::gemv_workspace_bytes(k, b);
+}
+
+int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                const uint16_t* x_fp16, int64_t b, float* y_f32, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !x_fp16 || !y_f32) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 8) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_fp16) || !aligned16(y_f32))
+    return LOWBIT_ERR_ALIGN;
+  const size_t need = lowbit::gemv_workspace_bytes(k, b);
+  if (!workspace || workspace_bytes < need) return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_gemv(fmt, static_cast<const uint8_t*>(codes), scales, n, k,
+                                        x_fp16, b, y_f32, workspace, stream));
+}
+
+static int gemm_common(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                       const uint16_t* x_bf16, int64_t m, void* y, bool out_f32,
+                       hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !x_bf16 || !y) return LOWBIT_ERR_ARG;
+  if (m < 1 || m > (int64_t(1) << 22)) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (m > kMaxElems / k || m > kMaxElems / n) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_bf16) || !aligned16(y))
+    return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_gemm(fmt, static_cast<const uint8_t*>(codes), scales, n, k,
+                                        x_bf16, m, y, out_f32, stream));
+}
+
+int lowbit_gemm(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                const uint16_t* x_bf16, int64_t m, uint16_t* y_bf16, hipStream_t stream) {
+  return gemm_common(fmt, codes, scales, n, k, x_bf16, m, y_bf16, false, stream);
+}
+
+int lowbit_gemm_f32(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                    const uint16_t* x_bf16, int64_t m, float* y_f32, hipStream_t stream) {
+  return gemm_common(fmt, codes, scales, n, k, x_bf16, m, y_f32, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+"""Thin ctypes binding of liblowbit.so (include/lowbit.h), same names.
+
+Argument marshalling only: every function checks tensor dtype / device /
+contiguity, allocates outputs when none are given (torch is the allocator),
+passes raw device pointers and torch's current HIP stream, and raises
+``LowbitError`` on a non-zero status.  All computation happens in the HIP
+kernels of the library.  If the library is missing this module raises on
+first use; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblowbit.so")
+
+LOWBIT_FMT_Q1_G128 = 1
+LOWBIT_FMT_T2_G128 = 2
+FORMATS = {"q1": LOWBIT_FMT_Q1_G128, "t2": LOWBIT_FMT_T2_G128}
+
+# exported symbols, in the order include/lowbit.h declares them
+SYMBOLS = [
+    "lowbit_version", "lowbit_status_str", "lowbit_codes_bytes", "lowbit_scales_bytes",
+    "lowbit_quantize_q1", "lowbit_pack_t2", "lowbit_pack", "lowbit_unpack",
+    "lowbit_gemv_workspace_bytes", "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32",
+]
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load liblowbit.so (built in-tree); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m bit_matmul_lowbit_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, sz, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "lowbit_version": ([], i),
+        "lowbit_status_str": ([i], ctypes.c_char_p),
+        "lowbit_codes_bytes": ([i, i64, i64], sz),
+        "lowbit_scales_bytes": ([i, i64, i64], sz),
+        "lowbit_quantize_q1": ([p, i64, i64, p, p, p], i),
+        "lowbit_pack_t2": ([p, p, i64, i64, p, p, p], i),
+        "lowbit_pack": ([i, p, p, i64, i64, p, p, p], i),
+        "lowbit_unpack": ([i, p, p, i64, i64, p, p], i),
+        "lowbit_gemv_workspace_bytes": ([i, i64, i64, i64], sz),
+        "lowbit_gemv": ([i, p, p, i64, i64, p, i64, p, p, sz, p], i),
+        "lowbit_gemm": ([i, p, p, i64, i64, p, i64, p, p], i),
+        "lowbit_gemm_f32": ([i, p, p, i64, i64, p, i64, p, p], i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().lowbit_status_str(int(status)).decode()
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LowbitError(status, where)
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtypes, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# host-only queries
+
+def lowbit_version() -> int:
+    return load().lowbit_version()
+
+
+def lowbit_codes_bytes(fmt, n: int, k: int) -> int:
+    return load().lowbit_codes_bytes(_fmt(fmt), n, k)
+
+
+def lowbit_scales_bytes(fmt, n: int, k: int) -> int:
+    return load().lowbit_scales_bytes(_fmt(fmt), n, k)
+
+
+def lowbit_gemv_workspace_bytes(fmt, n: int, k: int, b: int) -> int:
+    return load().lowbit_gemv_workspace_bytes(_fmt(fmt), n, k, b)
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+
+def _planes(fmt, n, k, device, codes, scales):
+    import torch
+
+    if codes is None:
+        codes = torch.empty(lowbit_codes_bytes(fmt, n, k), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty(lowbit_scales_bytes(fmt, n, k) // 2, dtype=torch.float16, device=device)
+    return codes, scales
+
+
+def lowbit_quantize_q1(w, codes=None, scales=None, stream=None):
+    """FP16 [n][k] -> (codes uint8, scales fp16) in the Q1 layout."""
+    import torch
+
+    n, k = w.shape
+    wp = _dev(w, (torch.float16,), "w")
+    codes, scales = _planes(LOWBIT_FMT_Q1_G128, n, k, w.device, codes, scales)
+    _check(load().lowbit_quantize_q1(wp, n, k, _dev(codes, (torch.uint8,), "codes"),
+                                     _dev(scales, (torch.float16, torch.int16), "scales"),
+                                     _stream(stream)), "lowbit_quantize_q1")
+    return codes, scales
+
+
+def lowbit_pack_t2(t, s, codes=None, scales=None, stream=None):
+    """int8 t [n][k] + FP16 group scales [n][k/128] -> (codes, scales)."""
+    import torch
+
+    n, k = t.shape
+    tp = _dev(t, (torch.int8,), "t")
+    sp = _dev(s, (torch.float16, torch.int16), "s")
+    if tuple(s.shape) != (n, k // 128):
+        raise ValueError("s must be [n][k/128]")
+    codes, scales = _planes(LOWBIT_FMT_T2_G128, n, k, t.device, codes, scales)
+    _check(load().lowbit_pack_t2(tp, sp, n, k, _dev(codes, (torch.uint8,), "codes"),
+                                 _dev(scales, (torch.float16, torch.int16), "scales"),
+                                 _stream(stream)), "lowbit_pack_t2")
+    return codes, scales
+
+
+def lowbit_pack(fmt, src, src_scales=None, codes=None, scales=None, stream=None):
+    if _fmt(fmt) == LOWBIT_FMT_Q1_G128:
+        if src_scales is not None:
+            raise ValueError("Q1 packing computes its scales; src_scales must be None")
+        return lowbit_quantize_q1(src, codes, scales, stream)
+    return lowbit_pack_t2(src, src_scales, codes, scales, stream)
+
+
+def lowbit_unpack(fmt, codes, scales, n: int, k: int, out=None, stream=None):
+    """codes + scales -> dense FP16 [n][k]."""
+    import torch
+
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float16, device=codes.device)
+    _check(load().lowbit_unpack(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                                _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                                _dev(out, (torch.float16, torch.int16), "out"), _stream(stream)),
+           "lowbit_unpack")
+    return out
+
+
+def lowbit_gemv(fmt, codes, scales, n: int, k: int, x, out=None, workspace=None, stream=None):
+    """x FP16 [b][k] (or [k]) -> y FP32 [b][n]."""
+    import torch
+
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    b = x2.shape[0]
+    if x2.shape[1] != k:
+        raise ValueError("x must have k columns")
+    if out is None:
+        out = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    need = lowbit_gemv_workspace_bytes(fmt, n, k, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(load().lowbit_gemv(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                              _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                              _dev(x2, (torch.float16,), "x"), b,
+                              _dev(out, (torch.float32,), "out"),
+                              _dev(workspace, (torch.uint8,), "workspace"),
+                              workspace.numel(), _stream(stream)), "lowbit_gemv")
+    return out
+
+
+def lowbit_gemm(fmt, codes, scales, n: int, k: int, x, out=None, stream=None):
+    """X BF16 [m][k] -> Y BF16 [m][n]."""
+    import torch
+
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _check(load().lowbit_gemm(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                              _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                              _dev(x, (torch.bfloat16,), "x"), m,
+                              _dev(out, (torch.bfloat16,), "out"), _stream(stream)), "lowbit_gemm")
+    return out
+
+
+def lowbit_gemm_f32(fmt, codes, scales, n: int, k: int, x, out=None, stream=None):
+    """X BF16 [m][k] -> Y FP32 [m][n] (same contraction, unrounded store)."""
+    import torch
+
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(load().lowbit_gemm_f32(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                                  _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                                  _dev(x, (torch.bfloat16,), "x"), m,
+                                  _dev(out, (torch.float32,), "out"), _stream(stream)),
+           "lowbit_gemm_f32")
+    return out

@@ -1,0 +1,154 @@
+"""GPU parity of the decode GEMV against the double-precision oracle.
+
+y[i][n] = sum_g s[n][g] * sum_{k in g} t[n][k] * x[i][k]  [P1 section 7; P2
+"Como funciona la compresion"].  FP32 outputs must stay within a floored
+relative error of 1e-3 (see helpers.floored_rel_err); one-hot inputs read a
+single weight back and must match bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_matmul_lowbit_amd import lowbit, synth
+from tests.helpers import assert_close, dev_u16, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _make(fmt, n, k, seed):
+    g = synth.rng(seed)
+    if fmt == "q1":
+        w = synth.fp16_normal(g, (n, k), 0.1)
+        codes, scales = oracle.q1_quantize(w)
+    else:
+        t = synth.ternary(g, (n, k))
+        s = synth.fp16_uniform(g, (n, k // 128), 0.01, 0.2)
+        codes, scales = oracle.t2_pack(t, s)
+    return g, codes, scales
+
+
+def _gemv(fmt, codes, scales, n, k, x16):
+    import torch
+
+    y = lowbit.lowbit_gemv(fmt, torch.from_numpy(codes).cuda(), dev_u16(scales), n, k, dev_u16(x16))
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("b", [1, 3, 8])
+def test_one_hot_reads_single_weight_exactly(fmt, b):
+    n, k = 70, 1280
+    say(f"gemv one-hot {fmt} b={b}")
+    g, codes, scales = _make(fmt, n, k, 500 + b)
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    dense = oracle.unpack(f, codes, scales, n, k).view(np.float16).astype(np.float64)
+    for cols in ([0] * b, list(range(7, 7 + 130 * b, 130)), [k - 1] * b, [511, 512, 513, 1000, 1279, 640, 3, 129][:b]):
+        x = np.zeros((b, k), np.uint16)
+        for i, c in enumerate(cols):
+            x[i, c] = 0x3C00
+        y = _gemv(fmt, codes, scales, n, k, x)
+        want = np.stack([dense[:, c] for c in cols])
+        assert np.array_equal(y, want), (cols, np.abs(y - want).max())
+
+
+SHAPES = [(1, 128), (16, 128), (37, 384), (300, 1280), (1000, 2176), (129, 4224)]
+
+
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 8])
+def test_small_shapes(fmt, n, k, b):
+    say(f"gemv {fmt} n={n} k={k} b={b}")
+    g, codes, scales = _make(fmt, n, k, 600 + n + k + b)
+    x = synth.fp16_normal(g, (b, k))
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.gemv(f, codes, scales, n, k, x)
+    y = _gemv(fmt, codes, scales, n, k, x)
+    assert_close(y, ref, f"{fmt} {n}x{k} b={b}")
+
+
+def test_zero_codes_and_zero_scales():
+    n, k = 40, 512
+    say("gemv zero codes / zero scales")
+    g = synth.rng(700)
+    s = synth.fp16_uniform(g, (n, k // 128), 0.01, 0.2)
+    codes, scales = oracle.t2_pack(np.zeros((n, k), np.int8), s)
+    x = synth.fp16_normal(g, (2, k))
+    assert not _gemv("t2", codes, scales, n, k, x).any()
+    w = synth.fp16_normal(g, (n, k), 0.1)
+    w[5] = 0  # all-zero row: scale 0, output exactly 0
+    codes, scales = oracle.q1_quantize(w)
+    y = _gemv("q1", codes, scales, n, k, x)
+    assert not y[:, 5].any()
+
+
+def test_repeated_calls_do_not_accumulate():
+    import torch
+
+    n, k = 256, 1024
+    say("gemv repeated calls")
+    g, codes, scales = _make("t2", n, k, 800)
+    x = dev_u16(synth.fp16_normal(g, (1, k)))
+    c, s = torch.from_numpy(codes).cuda(), dev_u16(scales)
+    ws = torch.empty(lowbit.lowbit_gemv_workspace_bytes("t2", n, k, 1), dtype=torch.uint8, device="cuda")
+    out = torch.full((1, n), 123.0, device="cuda")
+    y1 = lowbit.lowbit_gemv("t2", c, s, n, k, x, out=out, workspace=ws).clone()
+    y2 = lowbit.lowbit_gemv("t2", c, s, n, k, x, out=out, workspace=ws).clone()
+    torch.cuda.synchronize()
+    ref = oracle.gemv(oracle.T2, codes, scales, n, k, dev_host(x))
+    assert_close(y1.cpu().numpy(), ref)
+    assert_close(y2.cpu().numpy(), ref)
+
+
+def dev_host(x):
+    from tests.helpers import host_u16
+
+    return host_u16(x)
+
+
+# full-size decode shapes, generated on the device, every output row checked
+FULL = [
+    ("q1", 2048, 2048, 1),
+    ("t2", 6144, 2048, 1),
+    ("t2", 2048, 6144, 1),
+    ("q1", 34816, 5120, 1),
+    ("q1", 5120, 17408, 1),
+    ("q1", 34816, 5120, 5),
+    ("q1", 5120, 17408, 8),
+    ("t2", 151936, 5120, 1),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,b", FULL)
+def test_full_size(fmt, n, k, b):
+    import torch
+
+    from tests.helpers import host_u16, host_u8
+
+    say(f"gemv full {fmt} n={n} k={k} b={b}")
+    seed = 1000 + n + k + b
+    if fmt == "q1":
+        w = synth.dev_fp16_normal((n, k), 0.1, seed)
+        codes, scales = lowbit.lowbit_quantize_q1(w)
+        del w
+    else:
+        t = synth.dev_ternary((n, k), seed)
+        s = synth.dev_fp16_uniform((n, k // 128), 0.01, 0.2, seed + 1)
+        codes, scales = lowbit.lowbit_pack_t2(t, s)
+        del t, s
+    x = synth.dev_fp16_normal((b, k), 1.0, seed + 2)
+    y = lowbit.lowbit_gemv(fmt, codes, scales, n, k, x)
+    torch.cuda.synchronize()
+    hc, hs, hx = host_u8(codes), host_u16(scales), host_u16(x)
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    yh = y.cpu().numpy()
+    if b == 1:
+        ref = oracle.gemv(f, hc, hs, n, k, hx)
+        assert_close(yh, ref, f"full {fmt} {n}x{k}")
+    else:
+        rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(n - 64, n),
+                                         np.random.default_rng(1).integers(0, n, 512)]))
+        ref = np.concatenate([oracle.gemv(f, hc, hs, n, k, hx, row0=int(r0), nrows=1) for r0 in rows],
+                             axis=1)
+        assert_close(yh[:, rows], ref, f"full {fmt} {n}x{k} b={b} sampled rows")

@@ -1,0 +1,122 @@
+"""CPU checks of liblowbit.so: it loads, exports every symbol include/lowbit.h
+declares, answers its host-only queries, and rejects bad arguments on the host
+before any launch.  No call here reaches a kernel: every device entry point
+is called only with arguments that fail validation, so the tests run without
+a GPU.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from bit_matmul_lowbit_amd import lowbit
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lowbit.h")
+
+OK, ARG, SHAPE, ALIGN, UNSUP, HIP, WS = 0, 1, 2, 3, 4, 5, 6
+Q1, T2 = 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lowbit.LIB_PATH):
+        from bit_matmul_lowbit_amd import build
+
+        build.build()
+    return lowbit.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w \*]*?\b(lowbit_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_what_binding_lists():
+    assert declared_symbols() == lowbit.SYMBOLS
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lowbit_version() == 1
+    for s in range(7):
+        assert lowbit.status_str(s)
+    assert lowbit.status_str(99) == "unknown status"
+
+
+def test_size_queries(lib):
+    for n, k in [(2048, 2048), (151936, 5120), (34816, 5120), (5120, 17408), (37, 384)]:
+        np_ = (n + 15) // 16 * 16
+        assert lowbit.lowbit_codes_bytes("q1", n, k) == np_ * k // 8
+        assert lowbit.lowbit_codes_bytes("t2", n, k) == np_ * k // 4
+        assert lowbit.lowbit_scales_bytes("q1", n, k) == np_ * (k // 128) * 2
+        assert lowbit.lowbit_scales_bytes("t2", n, k) == np_ * (k // 128) * 2
+    # the pages' per-group byte counts: 18 B (1-bit), 34 B (2-bit ternary codes)
+    n, k = 4096, 4096
+    q1 = lowbit.lowbit_codes_bytes("q1", n, k) + lowbit.lowbit_scales_bytes("q1", n, k)
+    t2 = lowbit.lowbit_codes_bytes("t2", n, k) + lowbit.lowbit_scales_bytes("t2", n, k)
+    assert q1 == 18 * n * k // 128 and q1 * 8 / (n * k) == 1.125
+    assert t2 == 34 * n * k // 128 and t2 * 8 / (n * k) == 2.125
+    # bad formats / shapes give 0
+    assert lowbit.lowbit_codes_bytes(3, 16, 128) == 0
+    assert lowbit.lowbit_codes_bytes("q1", 0, 128) == 0
+    assert lowbit.lowbit_codes_bytes("q1", 16, 100) == 0
+    assert lowbit.lowbit_codes_bytes("q1", 16, 0) == 0
+    assert lowbit.lowbit_scales_bytes("t2", -1, 256) == 0
+
+
+def test_workspace_query(lib):
+    # one 64 KB table image per K-slice; a slice is 512/BP weights of K
+    for b, bp in [(1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)]:
+        k = 5120
+        slices = math.ceil((k // 8) / (64 // bp))
+        assert lowbit.lowbit_gemv_workspace_bytes("t2", 151936, k, b) == slices * 65536
+    assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, 128, 0) == 0
+    assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, 128, 9) == 0
+
+
+P = ctypes.c_void_p
+
+
+def test_validation_returns_before_launch(lib):
+    good = P(0x10000)  # never dereferenced: every call below fails validation
+    bad_align = P(0x10008)
+    null = P(0)
+    st = P(0)
+    # quantize
+    assert lib.lowbit_quantize_q1(null, 16, 128, good, good, st) == ARG
+    assert lib.lowbit_quantize_q1(good, 16, 100, good, good, st) == SHAPE
+    assert lib.lowbit_quantize_q1(good, 0, 128, good, good, st) == SHAPE
+    assert lib.lowbit_quantize_q1(bad_align, 16, 128, good, good, st) == ALIGN
+    # pack
+    assert lib.lowbit_pack_t2(good, null, 16, 128, good, good, st) == ARG
+    assert lib.lowbit_pack_t2(good, good, 16, 129, good, good, st) == SHAPE
+    assert lib.lowbit_pack_t2(good, good, 16, 128, bad_align, good, st) == ALIGN
+    assert lib.lowbit_pack(Q1, good, good, 16, 128, good, good, st) == ARG  # Q1 takes no scales
+    assert lib.lowbit_pack(7, good, null, 16, 128, good, good, st) == ARG
+    # unpack
+    assert lib.lowbit_unpack(0, good, good, 16, 128, good, st) == ARG
+    assert lib.lowbit_unpack(T2, good, good, 16, 64, good, st) == SHAPE
+    assert lib.lowbit_unpack(T2, good, bad_align, 16, 128, good, st) == ALIGN
+    # gemv
+    for b in (0, 9, -1):
+        assert lib.lowbit_gemv(Q1, good, good, 16, 128, good, b, good, good, 1 << 20, st) == ARG
+    assert lib.lowbit_gemv(Q1, good, good, 16, 120, good, 1, good, good, 1 << 20, st) == SHAPE
+    assert lib.lowbit_gemv(Q1, good, good, 16, 128, good, 1, bad_align, good, 1 << 20, st) == ALIGN
+    assert lib.lowbit_gemv(Q1, good, good, 16, 128, good, 1, good, null, 1 << 20, st) == WS
+    assert lib.lowbit_gemv(Q1, good, good, 16, 128, good, 1, good, good, 16, st) == WS
+    assert lib.lowbit_gemv(Q1, null, good, 16, 128, good, 1, good, good, 1 << 20, st) == ARG
+    # gemm
+    assert lib.lowbit_gemm(Q1, good, good, 16, 128, good, 0, good, st) == ARG
+    assert lib.lowbit_gemm(T2, good, good, 16, 130, good, 4, good, st) == SHAPE
+    assert lib.lowbit_gemm_f32(T2, good, good, 16, 128, bad_align, 4, good, st) == ALIGN
+    assert lib.lowbit_gemm_f32(T2, good, null, 16, 128, good, 4, good, st) == ARG
+    # a huge shape is refused, not overflowed
+    assert lib.lowbit_gemv(Q1, good, good, 1 << 40, 128, good, 1, good, good, 1 << 20, st) == SHAPE
