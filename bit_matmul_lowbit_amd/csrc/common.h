@@ -27,9 +27,11 @@ hipError_t launch_unpack(int fmt, const uint8_t* codes, const uint16_t* scales, 
                          int64_t k, uint16_t* w, hipStream_t st);
 
 size_t gemv_workspace_bytes(int64_t k, int64_t b);
-hipError_t launch_gemv(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
-                       int64_t k, const uint16_t* x, int64_t b, float* y, void* ws,
-                       hipStream_t st);
+hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
+                               void* ws, hipStream_t st);
+hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                  int64_t n, int64_t k, int64_t b, float* y, const void* ws,
+                                  hipStream_t st);
 
 hipError_t launch_gemm(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                        int64_t k, const uint16_t* x, int64_t m, void* y, bool out_f32,

@@ -307,21 +307,24 @@ size_t gemv_workspace_bytes(int64_t k, int64_t b) {
   return (size_t)nslices_for(k, ch) * kSliceFloats * sizeof(float);
 }
 
-hipError_t launch_gemv(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
-                       int64_t k, const uint16_t* x, int64_t b, float* y, void* ws,
-                       hipStream_t st) {
+hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
+                               void* ws, hipStream_t st) {
   const int ch = kLanes / bp_for(b);
   const int64_t nslices = nslices_for(k, ch);
-  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
-  float* lut = static_cast<float*>(ws);
-
   const int64_t build_threads = nslices * 16 * kLanes;
   const int64_t build_blocks = (build_threads + kWG - 1) / kWG;
   hipLaunchKernelGGL(gemv_build_kernel, dim3((unsigned)build_blocks), dim3(kWG), 0, st, x, k,
-                     (int)b, ch, nslices, lut, y, n * b);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                     (int)b, ch, nslices, static_cast<float*>(ws), y, n * b);
+  return hipGetLastError();
+}
 
+hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                  int64_t n, int64_t k, int64_t b, float* y, const void* ws,
+                                  hipStream_t st) {
+  const int ch = kLanes / bp_for(b);
+  const int64_t nslices = nslices_for(k, ch);
+  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
+  const float* lut = static_cast<const float*>(ws);
   // row blocks: enough work-groups to cover the GPU several times over, at
   // least two tiles per wave so the table copy is amortised
   const int64_t target_wgs = 4096;
@@ -330,7 +333,8 @@ hipError_t launch_gemv(int fmt, const uint8_t* codes, const uint16_t* scales, in
   if (rb < 8) rb = 8;
   nrb = (ntiles + rb - 1) / rb;
   dim3 grid((unsigned)nrb, (unsigned)nslices);
-  if (fmt == 1) return launch_main<1>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, (int)rb);
+  if (fmt == 1)
+    return launch_main<1>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, (int)rb);
   return launch_main<2>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, (int)rb);
 }
 

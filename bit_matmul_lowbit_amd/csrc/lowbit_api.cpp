@@ -99,6 +99,32 @@ size_t lowbit_gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b) {
   return lowbit::gemv_workspace_bytes(k, b);
 }
 
+int lowbit_gemv_prepare(int64_t n, int64_t k, const uint16_t* x_fp16, int64_t b, float* y_f32,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x_fp16 || !y_f32) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 8) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(x_fp16) || !aligned16(y_f32)) return LOWBIT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lowbit::gemv_workspace_bytes(k, b))
+    return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_gemv_prepare(n, k, x_fp16, b, y_f32, workspace, stream));
+}
+
+int lowbit_gemv_accumulate(int fmt, const void* codes, const uint16_t* scales, int64_t n,
+                           int64_t k, int64_t b, float* y_f32, const void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !y_f32) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 8) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y_f32)) return LOWBIT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lowbit::gemv_workspace_bytes(k, b))
+    return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_gemv_accumulate(fmt, static_cast<const uint8_t*>(codes),
+                                                   scales, n, k, b, y_f32, workspace, stream));
+}
+
 int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
                 const uint16_t* x_fp16, int64_t b, float* y_f32, void* workspace,
                 size_t workspace_bytes, hipStream_t stream) {
@@ -107,11 +133,10 @@ int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales, int64_t n, i
   if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_fp16) || !aligned16(y_f32))
     return LOWBIT_ERR_ALIGN;
-  const size_t need = lowbit::gemv_workspace_bytes(k, b);
-  if (!workspace || workspace_bytes < need) return LOWBIT_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
-  return hip_status(lowbit::launch_gemv(fmt, static_cast<const uint8_t*>(codes), scales, n, k,
-                                        x_fp16, b, y_f32, workspace, stream));
+  const int st = lowbit_gemv_prepare(n, k, x_fp16, b, y_f32, workspace, workspace_bytes, stream);
+  if (st != LOWBIT_OK) return st;
+  return lowbit_gemv_accumulate(fmt, codes, scales, n, k, b, y_f32, workspace, workspace_bytes,
+                                stream);
 }
 
 static int gemm_common(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,

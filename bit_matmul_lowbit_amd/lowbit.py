@@ -23,7 +23,8 @@ FORMATS = {"q1": LOWBIT_FMT_Q1_G128, "t2": LOWBIT_FMT_T2_G128}
 SYMBOLS = [
     "lowbit_version", "lowbit_status_str", "lowbit_codes_bytes", "lowbit_scales_bytes",
     "lowbit_quantize_q1", "lowbit_pack_t2", "lowbit_pack", "lowbit_unpack",
-    "lowbit_gemv_workspace_bytes", "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32",
+    "lowbit_gemv_workspace_bytes", "lowbit_gemv_prepare", "lowbit_gemv_accumulate",
+    "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32",
 ]
 
 
@@ -57,6 +58,8 @@ def load() -> ctypes.CDLL:
         "lowbit_pack": ([i, p, p, i64, i64, p, p, p], i),
         "lowbit_unpack": ([i, p, p, i64, i64, p, p], i),
         "lowbit_gemv_workspace_bytes": ([i, i64, i64, i64], sz),
+        "lowbit_gemv_prepare": ([i64, i64, p, i64, p, p, sz, p], i),
+        "lowbit_gemv_accumulate": ([i, p, p, i64, i64, i64, p, p, sz, p], i),
         "lowbit_gemv": ([i, p, p, i64, i64, p, i64, p, p, sz, p], i),
         "lowbit_gemm": ([i, p, p, i64, i64, p, i64, p, p], i),
         "lowbit_gemm_f32": ([i, p, p, i64, i64, p, i64, p, p], i),
@@ -203,6 +206,33 @@ def lowbit_gemv(fmt, codes, scales, n: int, k: int, x, out=None, workspace=None,
                               _dev(out, (torch.float32,), "out"),
                               _dev(workspace, (torch.uint8,), "workspace"),
                               workspace.numel(), _stream(stream)), "lowbit_gemv")
+    return out
+
+
+def lowbit_gemv_prepare(n: int, k: int, x, out, workspace, stream=None):
+    """Tables for x FP16 [b][k] into `workspace`; out FP32 [b][n] := 0."""
+    import torch
+
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    b = x2.shape[0]
+    _check(load().lowbit_gemv_prepare(n, k, _dev(x2, (torch.float16,), "x"), b,
+                                      _dev(out, (torch.float32,), "out"),
+                                      _dev(workspace, (torch.uint8,), "workspace"),
+                                      workspace.numel(), _stream(stream)), "lowbit_gemv_prepare")
+    return out
+
+
+def lowbit_gemv_accumulate(fmt, codes, scales, n: int, k: int, b: int, out, workspace,
+                           stream=None):
+    """out FP32 [b][n] += W.x with the tables left by lowbit_gemv_prepare."""
+    import torch
+
+    _check(load().lowbit_gemv_accumulate(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                                         _dev(scales, (torch.float16, torch.int16), "scales"),
+                                         n, k, b, _dev(out, (torch.float32,), "out"),
+                                         _dev(workspace, (torch.uint8,), "workspace"),
+                                         workspace.numel(), _stream(stream)),
+           "lowbit_gemv_accumulate")
     return out
 
 

@@ -113,6 +113,13 @@ def test_validation_returns_before_launch(lib):
     assert lib.lowbit_gemv(Q1, good, good, 16, 128, good, 1, good, null, 1 << 20, st) == WS
     assert lib.lowbit_gemv(Q1, good, good, 16, 128, good, 1, good, good, 16, st) == WS
     assert lib.lowbit_gemv(Q1, null, good, 16, 128, good, 1, good, good, 1 << 20, st) == ARG
+    assert lib.lowbit_gemv_prepare(16, 128, null, 1, good, good, 1 << 20, st) == ARG
+    assert lib.lowbit_gemv_prepare(16, 128, good, 9, good, good, 1 << 20, st) == ARG
+    assert lib.lowbit_gemv_prepare(16, 136, good, 1, good, good, 1 << 20, st) == SHAPE
+    assert lib.lowbit_gemv_prepare(16, 128, good, 1, good, good, 8, st) == WS
+    assert lib.lowbit_gemv_accumulate(0, good, good, 16, 128, 1, good, good, 1 << 20, st) == ARG
+    assert lib.lowbit_gemv_accumulate(T2, good, good, 16, 128, 1, bad_align, good, 1 << 20, st) == ALIGN
+    assert lib.lowbit_gemv_accumulate(T2, good, good, 16, 128, 1, good, null, 1 << 20, st) == WS
     # gemm
     assert lib.lowbit_gemm(Q1, good, good, 16, 128, good, 0, good, st) == ARG
     assert lib.lowbit_gemm(T2, good, good, 16, 130, good, 4, good, st) == SHAPE
