@@ -9,29 +9,28 @@
 // Method: lookup tables of signed subset sums (the T-MAC idea of Wei et al.,
 // 2024, redone for CDNA4's LDS).  For one 8-weight chunk of x,
 //     S[e] = sum_{j<8} (bit j of e ? +x_j : -x_j),  e = 0..255.
-// A Q1 code byte e of row n then contributes s * S[e].  A ternary chunk with
-// pos byte p and neg byte q contributes s * (M[p] - M[q]) with M the masked
-// subset sums, and M[p] - M[q] = (S[p] - S[q]) / 2, so one table serves both
-// codes (the 1/2 is applied once per output).
+// A Q1 code byte e of row n then contributes S[e]; a ternary chunk with pos
+// byte p and neg byte q contributes M[p] - M[q] (M = masked subset sums), and
+// M[p] - M[q] = (S[p] - S[q]) / 2, so one table serves both codes (the 1/2 is
+// applied once per output).  The group scale multiplies the per-group sum.
 //
 // Data flow per call:
-//   1. build kernel: every table S for every (column, chunk) into the
-//      workspace, laid out exactly as the LDS image the main kernel wants;
-//      it also zeroes y.
-//   2. main kernel: a work-group owns one K-slice (the chunks held by its 64
-//      lanes) and a range of 16-row tiles.  It copies the slice's 64 KB table
-//      image into LDS once, then each wave streams 16-row code cells: lane l
-//      loads the 16 B (Q1) / 32 B (T2) cell of its chunk, so a wave reads
-//      1-2 KB contiguous per tile.  Each code byte becomes one LDS lookup
-//      whose address is (byte << 8) | (lane << 2), built by one v_perm_b32:
-//      table entry e of lane l sits at e*256 + 4*l, so every lane reads its
-//      own bank -- conflict free.  Per-lane partial sums of the 16 rows are
-//      then reduced across the lanes of the slice by a transposed butterfly
-//      (permlane32/16 swaps, DPP row rotates / mirrors / quad perms) and
-//      added to y with one atomic per row and K-slice.
+//   1. build kernel (lowbit_gemv_prepare): every table S into the workspace,
+//      laid out exactly as the LDS image the main kernel copies; zeroes y.
+//   2. main kernel (lowbit_gemv_accumulate): a work-group holds one K-slice:
+//      each lane owns two adjacent chunks of one group (two 64 KB tables,
+//      128 KB of LDS), and eight neighbouring lanes cover one group.  Per
+//      16-row tile a lane loads its 32 B (Q1) / 64 B (T2) of codes and one
+//      dword of scales; each code byte becomes one LDS lookup at
+//      (byte << 8) | (lane << 2) | (table << 16) -- a single v_perm_b32; every
+//      lane reads its own bank, conflict-free.  The 16 row partials are then
+//      reduced over the lanes of the same group (permlane swaps / DPP, three
+//      transposed stages leave two rows per lane), multiplied by those two
+//      rows' scales, reduced over the groups, and added to y with one FP32
+//      atomic per row and K-slice.
 //
 // With batch b > 1 the 64 lanes are split into BP = 2, 4, 8 column groups of
-// CH = 64 / BP chunks (BP = b rounded up to a power of two); the code cells
+// CH = 64 / BP lanes (BP = b rounded up to a power of two); the code cells
 // are then re-read by each column group from cache, and the VALU work grows
 // with BP.  No matrix cores: this is a streaming, not a dense, contraction.
 #include "common.h"
@@ -65,22 +64,32 @@ constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 
 // ---------------------------------------------------------------------------
-// build: tables of signed subset sums, one thread per (slice, hi nibble, lane)
+// Lane -> chunk map of the main kernel.  Within a column group of CH lanes,
+// lane l' = 8 j + i (i = l' % 8, j = l' / 8 < GW = CH / 8) owns chunks
+// s * 2CH + 16 j + 2 i + q (q = 0, 1) of slice s: two adjacent chunks of
+// group s * GW + j.  Eight neighbouring lanes thus cover one 128-weight group
+// and read 256 (Q1) / 512 (T2) contiguous bytes of a tile.
+
+__device__ __forceinline__ int64_t lane_chunk(int64_t s, int lanec, int ch, int q) {
+  return s * 2 * ch + 16 * (lanec >> 3) + 2 * (lanec & 7) + q;
+}
+
+// build: table images, one thread per (image = slice*2 + q, hi nibble, lane)
 
 __global__ __launch_bounds__(kWG) void gemv_build_kernel(const uint16_t* __restrict__ x, int64_t k,
-                                                         int b, int ch, int64_t nslices,
+                                                         int b, int ch, int64_t nimages,
                                                          float* __restrict__ lut,
                                                          float* __restrict__ y, int64_t ycount) {
   const int64_t gid = (int64_t)blockIdx.x * kWG + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kWG;
   for (int64_t i = gid; i < ycount; i += stride) y[i] = 0.0f;
-  if (gid >= nslices * 16 * kLanes) return;
+  if (gid >= nimages * 16 * kLanes) return;
   const int lane = (int)(gid & 63);
   const int hi = (int)((gid >> 6) & 15);
-  const int64_t s = gid >> 10;
+  const int64_t img = gid >> 10;
   const int col = lane / ch;
-  const int64_t chunk = s * ch + lane % ch;
-  float* dst = lut + (s * kEntries + hi * 16) * kLanes + lane;
+  const int64_t chunk = lane_chunk(img >> 1, lane % ch, ch, (int)(img & 1));
+  float* dst = lut + (img * kEntries + hi * 16) * kLanes + lane;
   if (col >= b || chunk >= k / kChunk) {
 #pragma unroll
     for (int lo = 0; lo < 16; ++lo) dst[lo * kLanes] = 0.0f;
@@ -104,9 +113,7 @@ __global__ __launch_bounds__(kWG) void gemv_build_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// cross-lane reduction of 16 per-lane row partials over the CH chunk lanes
-// (lane bits 0 .. log2(CH)-1).  After it, slot j of a lane holds the full
-// sum of row (row_off + j); `writer` marks one lane per (column, row).
+// Cross-lane reduction of 16 per-lane row partials.
 
 template <int STAGE_BIT>
 __device__ __forceinline__ float partner(float v) {
@@ -116,7 +123,11 @@ __device__ __forceinline__ float partner(float v) {
   else return dpp<kQuadXor1>(v);
 }
 
-// transposed stage on lane bit P: m values -> m/2 values
+// Transposed stage on lane bit P: M values -> M/2 values.  The lane with bit
+// P clear keeps the low half of the rows, its partner the high half.  The
+// bit-2 partner (half mirror) also flips bits 1 and 0; that is harmless as
+// long as stages on bits 1 and 0 follow and the lanes involved hold partials
+// that may be summed unscaled (same 128-weight group).
 template <int P, int M>
 __device__ __forceinline__ void tstage(float (&v)[16], int lane, int& row_off) {
   const bool hi = (lane >> P) & 1;
@@ -144,44 +155,52 @@ __device__ __forceinline__ void tstage(float (&v)[16], int lane, int& row_off) {
   row_off += hi ? M / 2 : 0;
 }
 
+// Butterfly on lane bit P (3, 4 or 5): v[0] summed with the partner lane's.
 template <int P>
 __device__ __forceinline__ void bstage(float (&v)[16]) {
-  v[0] = v[0] + partner<P>(v[0]);
+  if constexpr (P == 5) {
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(v[0]), f2u(v[0]), false, false);
+    v[0] = u2f(r[0]) + u2f(r[1]);
+  } else if constexpr (P == 4) {
+    auto r = __builtin_amdgcn_permlane16_swap(f2u(v[0]), f2u(v[0]), false, false);
+    v[0] = u2f(r[0]) + u2f(r[1]);
+  } else {
+    v[0] = v[0] + partner<P>(v[0]);
+  }
 }
 
-// returns number of valid slots; row of slot j is row_off + j
-template <int CH>
-__device__ __forceinline__ int reduce_rows(float (&v)[16], int lane, int& row_off, bool& writer) {
+// Part 1, within a group (lane bits 2..0 = i): three transposed stages leave
+// rows row_off and row_off + 1 in v[0], v[1], with row_off = 2 (lane % 8).
+__device__ __forceinline__ void reduce_in_group(float (&v)[16], int lane, int& row_off) {
   row_off = 0;
+  tstage<2, 16>(v, lane, row_off);
+  tstage<1, 8>(v, lane, row_off);
+  tstage<0, 4>(v, lane, row_off);
+}
+
+// Part 2, across the GW groups of the slice (lane bits log2(CH)-1 .. 3 = j),
+// after each lane has scaled its two rows.  Returns the number of valid
+// slots; slot t holds row row_off + t; `writer` marks one lane per
+// (column, row).
+template <int CH>
+__device__ __forceinline__ int reduce_groups(float (&v)[16], int lane, int& row_off, bool& writer) {
   if constexpr (CH == 64) {
-    tstage<5, 16>(v, lane, row_off);
-    tstage<4, 8>(v, lane, row_off);
-    tstage<3, 4>(v, lane, row_off);
-    tstage<2, 2>(v, lane, row_off);
-    bstage<1>(v);
-    bstage<0>(v);
-    writer = (lane & 3) == 0;
+    tstage<5, 2>(v, lane, row_off);
+    bstage<4>(v);
+    bstage<3>(v);
+    writer = (lane & 0x18) == 0;
     return 1;
   } else if constexpr (CH == 32) {
-    tstage<4, 16>(v, lane, row_off);
-    tstage<3, 8>(v, lane, row_off);
-    tstage<2, 4>(v, lane, row_off);
-    tstage<1, 2>(v, lane, row_off);
-    bstage<0>(v);
-    writer = (lane & 1) == 0;
+    tstage<4, 2>(v, lane, row_off);
+    bstage<3>(v);
+    writer = (lane & 0x08) == 0;
     return 1;
   } else if constexpr (CH == 16) {
-    tstage<3, 16>(v, lane, row_off);
-    tstage<2, 8>(v, lane, row_off);
-    tstage<1, 4>(v, lane, row_off);
-    tstage<0, 2>(v, lane, row_off);
+    tstage<3, 2>(v, lane, row_off);
     writer = true;
     return 1;
   } else {
     static_assert(CH == 8, "CH must be 64, 32, 16 or 8");
-    tstage<2, 16>(v, lane, row_off);
-    tstage<1, 8>(v, lane, row_off);
-    tstage<0, 4>(v, lane, row_off);
     writer = true;
     return 2;
   }
@@ -198,17 +217,18 @@ __device__ __forceinline__ uint32_t entry_addr(uint32_t word, uint32_t lane_base
 // ---------------------------------------------------------------------------
 // main kernel
 
-constexpr int kMainWaves = 12;                  // one 768-thread work-group per CU
+constexpr int kMainWaves = 16;                  // one 1024-thread work-group per CU
 constexpr int kMainThreads = kMainWaves * 64;
-constexpr int kCpl = 2;                         // chunks (tables) per lane per slice
+constexpr int kImages = 2;                      // tables per lane (chunks q = 0, 1)
 
-// tiles of code loads in flight per wave
-template <int FMT> constexpr int kDepth = FMT == 1 ? 3 : 2;
+// 16-byte code cells per lane per tile, and tiles of loads in flight per wave
+template <int FMT> constexpr int kCells = FMT == 1 ? 2 : 4;
+template <int FMT, int CH> constexpr int kDepth = FMT == 1 ? 4 : 3;
 
 template <int FMT>
 struct TileRegs {
-  uint4 pa[kCpl], na[kCpl];  // code cells: Q1 16 B (pa) / T2 pos (pa) + neg (na)
-  uint4 s0[kCpl], s1[kCpl];  // 16 FP16 scales of the tile's rows for each chunk's group
+  uint4 c[kCells<FMT>];  // Q1: chunk 0, chunk 1; T2: pos 0, neg 0, pos 1, neg 1
+  uint32_t sc;           // FP16 scales of this lane's two rows for its group
 };
 
 // Tile loads go through buffer resources whose base is the tile's row of
@@ -224,57 +244,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
                                            kRawBufferFlags);
 }
 
+// `off` is the per-lane (VGPR) offset, SOFF a constant added by the
+// instruction itself (no extra VGPR per cell)
+template <int SOFF = 0>
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, SOFF, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int FMT>
 __device__ __forceinline__ void load_tile(TileRegs<FMT>& r, __amdgpu_buffer_rsrc_t cr,
-                                          __amdgpu_buffer_rsrc_t sr, const uint32_t (&coff)[kCpl],
-                                          const uint32_t (&soff)[kCpl]) {
-#pragma unroll
-  for (int q = 0; q < kCpl; ++q) {
-    r.pa[q] = bload(cr, coff[q]);
-    if constexpr (FMT == 2) r.na[q] = bload(cr, coff[q] + 16);
-    r.s0[q] = bload(sr, soff[q]);
-    r.s1[q] = bload(sr, soff[q] + 16);
+                                          __amdgpu_buffer_rsrc_t sr, uint32_t coff, uint32_t soff) {
+  r.c[0] = bload<0>(cr, coff);
+  r.c[1] = bload<16>(cr, coff);
+  if constexpr (kCells<FMT> == 4) {
+    r.c[2] = bload<32>(cr, coff);
+    r.c[3] = bload<48>(cr, coff);
   }
+  r.sc = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, 0, 0);
 }
 
-// Lookups of one 16-row tile: acc[r] = sum over this lane's chunks of
-// s[r] * S[code byte] (T2: s[r] * (S[pos] - S[neg])).  Branch-free: lanes
-// without a chunk (a partial last K-slice, or columns beyond b) read their
-// own all-zero table and, when MASKED, get zero scales, so they add exact
-// zeros.
-template <int FMT, bool MASKED>
-__device__ __forceinline__ void tile_lookups(const TileRegs<FMT>& tr, const bool (&active)[kCpl],
-                                             const char* tbase, const uint32_t (&lane_base)[kCpl],
-                                             float (&acc)[16]) {
+// Lookups of one 16-row tile: acc[r] = sum over this lane's two chunks of
+// S[code byte of row r] (T2: S[pos] - S[neg]).  Unscaled: both chunks belong
+// to the same group.  Lanes without a chunk (past the end of K, or a column
+// beyond b) read their own all-zero tables.
+template <int FMT>
+__device__ __forceinline__ void tile_lookups(const TileRegs<FMT>& tr, const char* tbase,
+                                             uint32_t lane_base, float (&acc)[16]) {
 #pragma unroll
-  for (int q = 0; q < kCpl; ++q) {
-    const uint32_t pw[4] = {tr.pa[q].x, tr.pa[q].y, tr.pa[q].z, tr.pa[q].w};
+  for (int q = 0; q < kImages; ++q) {
+    const uint4 pc = tr.c[FMT == 1 ? q : 2 * q];
+    const uint32_t pw[4] = {pc.x, pc.y, pc.z, pc.w};
     uint32_t nw[4] = {0u, 0u, 0u, 0u};
     if constexpr (FMT == 2) {
-      nw[0] = tr.na[q].x; nw[1] = tr.na[q].y; nw[2] = tr.na[q].z; nw[3] = tr.na[q].w;
+      const uint4 nc = tr.c[2 * q + 1];
+      nw[0] = nc.x; nw[1] = nc.y; nw[2] = nc.z; nw[3] = nc.w;
     }
-    uint32_t sw[8] = {tr.s0[q].x, tr.s0[q].y, tr.s0[q].z, tr.s0[q].w,
-                      tr.s1[q].x, tr.s1[q].y, tr.s1[q].z, tr.s1[q].w};
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sw[i] = active[q] ? sw[i] : 0u;
-    }
-    const uint32_t lb = lane_base[q];
+    const uint32_t lb = lane_base | ((uint32_t)q << 16);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #define LOWBIT_ROW(J)                                                                   \
   {                                                                                     \
     const int r = w * 4 + J;                                                            \
-    const float sc = h2f((sw[r >> 1] >> ((r & 1) * 16)) & 0xFFFFu);                     \
     float val = *reinterpret_cast<const float*>(tbase + entry_addr<J>(pw[w], lb));      \
     if constexpr (FMT == 2)                                                             \
       val -= *reinterpret_cast<const float*>(tbase + entry_addr<J>(nw[w], lb));         \
-    acc[r] = (q == 0) ? sc * val : __builtin_fmaf(sc, val, acc[r]);                     \
+    acc[r] = (q == 0) ? val : acc[r] + val;                                             \
   }
       LOWBIT_ROW(0)
       LOWBIT_ROW(1)
@@ -285,37 +300,42 @@ __device__ __forceinline__ void tile_lookups(const TileRegs<FMT>& tr, const bool
   }
 }
 
-// Cross-lane reduction of a tile's 16 row partials and one atomic add per
-// row (skipped for tiles past the end: `live` is wave-uniform).
+// Reduction of a tile's 16 row partials: within the group, scale the two
+// rows each lane is left with (scale word `sw`, zero for inactive lanes),
+// across the groups, then one atomic add per row (skipped for tiles past the
+// end: `live` is wave-uniform).  T2 halves its sums here.
 template <int FMT, int CH>
-__device__ __forceinline__ void tile_store(float (&acc)[16], bool live, int lane, int col, int b,
-                                           int64_t t, int64_t n, float* __restrict__ y) {
+__device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, bool live, int lane,
+                                           int col, int b, int64_t t, int64_t n,
+                                           float* __restrict__ y) {
   int row_off;
   bool writer;
-  const int nv = reduce_rows<CH>(acc, lane, row_off, writer);
+  reduce_in_group(acc, lane, row_off);
   const float half = (FMT == 2) ? 0.5f : 1.0f;
+  acc[0] *= h2f(sw & 0xFFFFu) * half;
+  acc[1] *= h2f(sw >> 16) * half;
+  const int nv = reduce_groups<CH>(acc, lane, row_off, writer);
 #pragma unroll
   for (int j = 0; j < nv; ++j) {
     const int64_t row = t * kTileRows + row_off + j;
-    if (live && writer && col < b && row < n) atomicAdd(y + (int64_t)col * n + row, acc[j] * half);
+    if (live && writer && col < b && row < n) atomicAdd(y + (int64_t)col * n + row, acc[j]);
   }
 }
 
-// Work decomposition.  A slice is kCpl consecutive sub-slices of CH chunks
-// (a sub-slice is what one 64 KB table image covers); lane l holds chunk
-// l % CH of each of them.  The grid is G x nslices work-groups: work-group j
-// keeps slice s = j % nslices (one copy of its tables) and the row-tile
-// blocks m, m + G, m + 2G, ... (m = j / nslices; 16 tiles per block, one per
-// wave).  At any moment all work-groups are near the same block index, so
-// the chip sweeps the code plane front to back in one contiguous front: HBM
-// serves such a sweep measurably faster (about 6.3 TB/s on MI355X) than
-// hundreds of independent streams (about 4.8 TB/s).
+// Work decomposition.  A slice is 2 CH consecutive chunks (GW = CH / 8
+// groups); the grid is G x nslices work-groups: work-group w keeps slice
+// s = w % nslices (one copy of its two table images in LDS) and the
+// row-tile blocks m, m + G, m + 2G, ... (m = w / nslices; 16 tiles per
+// block, one per wave).  At any moment all work-groups are near the same
+// block index, so the chip sweeps the code plane front to back in one
+// contiguous front: HBM serves such a sweep measurably faster (about
+// 6.3 TB/s on MI355X) than hundreds of independent streams (about 4.8 TB/s).
 template <int FMT, int CH>
-__global__ __launch_bounds__(kMainThreads, 3) void gemv_main_kernel(
+__global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const float* __restrict__ lut, float* __restrict__ y, int64_t n, int64_t k, int b,
-    int64_t ntiles, int64_t nsub, int64_t nslices) {
-  __shared__ float4 table[kCpl * kSliceFloats / 4];
+    int64_t ntiles, int64_t nslices) {
+  __shared__ float4 table[kImages * kSliceFloats / 4];
   const int64_t s = blockIdx.x % nslices;
   const int64_t m = blockIdx.x / nslices;
   const int64_t G = gridDim.x / nslices;
@@ -323,77 +343,83 @@ __global__ __launch_bounds__(kMainThreads, 3) void gemv_main_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane / CH;
-  const int64_t chunks = k / kChunk;
+  const int i8 = lane & 7;
   const int64_t groups = k / kGroup;
   const char* tbase = reinterpret_cast<const char*>(table);
   constexpr int S = kMainWaves;
+  constexpr int GW = CH / 8;
 
-  bool active[kCpl];
-  uint32_t coff[kCpl], soff[kCpl], lane_base[kCpl];
-  bool full = b * CH >= kLanes;  // wave-uniform: every lane holds a chunk of a real column
-#pragma unroll
-  for (int q = 0; q < kCpl; ++q) {
-    const int64_t sub = s * kCpl + q;
-    const int64_t c = sub * CH + lane % CH;
-    active[q] = (col < b) && (c < chunks);
-    full = full && (sub * CH + CH <= chunks);
-    // every lane loads from a valid chunk; inactive lanes are masked later
-    const int64_t cl = c < chunks ? c : chunks - 1;
-    coff[q] = (uint32_t)(cl * Fmt<FMT>::cell_bytes);
-    soff[q] = (uint32_t)((cl / kChunksPerGroup) * kTileRows * 2);
-    lane_base[q] = (uint32_t)lane * 4u | ((uint32_t)q << 16);
-  }
+  // this lane's group; every lane loads from a valid group, inactive lanes
+  // read zero tables and get a zero scale word
+  const int64_t g = s * GW + ((lane % CH) >> 3);
+  const bool active = (col < b) && (g < groups);
+  const int64_t gc = g < groups ? g : groups - 1;
+  const uint32_t coff = (uint32_t)((gc * kChunksPerGroup + 2 * i8) * Fmt<FMT>::cell_bytes);
+  const uint32_t soff = (uint32_t)((gc * kTileRows + 2 * i8) * 2);
+  const uint32_t lane_base = (uint32_t)lane * 4u;
+
   const int stride = (int)(G * S);  // tiles between a wave's tiles
   const int tb = (int)ntiles;
-  const int64_t cpitch = chunks * Fmt<FMT>::cell_bytes;  // bytes per 16-row tile
-  const int64_t spitch = groups * kTileRows * 2;
-  const uint8_t* cbase = codes;
-  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(scales);
-  auto crs = [&](int t) { return t < tb ? tile_rsrc(cbase + t * cpitch, cpitch) : tile_rsrc(cbase, 0); };
-  auto srs = [&](int t) { return t < tb ? tile_rsrc(sbase + t * spitch, spitch) : tile_rsrc(sbase, 0); };
+  const int cpitch = (int)((k / kChunk) * Fmt<FMT>::cell_bytes);  // bytes per 16-row tile
+  const int spitch = (int)(groups * kTileRows * 2);
   int t = (int)(m * S) + wave;
+  // Running (scalar) bases of the next tile to load.  A tile past the end
+  // gets a zero-length resource: its loads return zeros and touch nothing,
+  // so its base may point past the arrays.
+  int tn = t;
+  const uint8_t* cn = codes + (int64_t)tn * cpitch;
+  const uint8_t* sn = reinterpret_cast<const uint8_t*>(scales) + (int64_t)tn * spitch;
+  const int64_t cstep = (int64_t)stride * cpitch, sstep = (int64_t)stride * spitch;
+  auto load_next = [&](TileRegs<FMT>& r) {
+    const bool in = tn < tb;
+    load_tile<FMT>(r, tile_rsrc(cn, in ? cpitch : 0), tile_rsrc(sn, in ? spitch : 0), coff, soff);
+    tn += stride;
+    cn += cstep;
+    sn += sstep;
+  };
+
+  // The slice's two table images (the build kernel zero-fills lanes without
+  // a chunk, so every entry read is finite) are loaded into registers first
+  // and written to LDS after the first tiles' loads are issued: loads
+  // complete in issue order, so the tables are not queued behind the tiles.
+  constexpr int kTableVecs = kImages * kSliceFloats / 4 / kMainThreads;
+  uint4 tv[kTableVecs];
+  {
+    const __amdgpu_buffer_rsrc_t lr = tile_rsrc(reinterpret_cast<const uint8_t*>(lut + s * kImages * kSliceFloats),
+                                                kImages * kSliceFloats * 4);
+#pragma unroll
+    for (int i = 0; i < kTableVecs; ++i) tv[i] = bload<0>(lr, (threadIdx.x + i * kMainThreads) * 16u);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ring of D register sets: the loads of the next D-1 tiles of this wave
   // are in flight while one tile is contracted
-  constexpr int D = kDepth<FMT>;
+  constexpr int D = kDepth<FMT, CH>;
   TileRegs<FMT> buf[D];
 #pragma unroll
-  for (int i = 0; i < D - 1; ++i) load_tile<FMT>(buf[i], crs(t + i * stride), srs(t + i * stride), coff, soff);
-  {
-    // table images of this slice's sub-slices; a sub-slice past the end of K
-    // gets an all-zero region, so its (inactive) lanes read finite zeros
+  for (int i = 0; i < D - 1; ++i) load_next(buf[i]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < kCpl; ++q) {
-      const int64_t sub = s * kCpl + q;
-      if (sub < nsub) {
-        const float4* src = reinterpret_cast<const float4*>(lut + sub * kSliceFloats);
-#pragma unroll
-        for (int i = threadIdx.x; i < kSliceFloats / 4; i += kMainThreads)
-          table[q * (kSliceFloats / 4) + i] = src[i];
-      } else {
-        for (int i = threadIdx.x; i < kSliceFloats / 4; i += kMainThreads)
-          table[q * (kSliceFloats / 4) + i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  }
+  for (int i = 0; i < kTableVecs; ++i)
+    table[threadIdx.x + i * kMainThreads] = __builtin_bit_cast(float4, tv[i]);
   __syncthreads();
 
-  // software pipeline: the lookups of tile t + stride are issued next to the
-  // reduction of tile t, two independent dependency chains
+  // software pipeline: the lookups of the next tile are issued next to the
+  // reduction of the current one, two independent dependency chains
   float acc0[16], acc1[16];
-  if (full) tile_lookups<FMT, false>(buf[0], active, tbase, lane_base, acc0);
-  else tile_lookups<FMT, true>(buf[0], active, tbase, lane_base, acc0);
+  tile_lookups<FMT>(buf[0], tbase, lane_base, acc0);
+  uint32_t sw_cur = active ? buf[0].sc : 0u;
   constexpr int U = (D % 2 == 0) ? D : 2 * D;  // multiple of the ring and of 2
   while (t < tb) {
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       float (&cur)[16] = (i & 1) ? acc1 : acc0;
       float (&nxt)[16] = (i & 1) ? acc0 : acc1;
-      const int tn = t + (D - 1) * stride;
-      load_tile<FMT>(buf[(i + D - 1) % D], crs(tn), srs(tn), coff, soff);
-      if (full) tile_lookups<FMT, false>(buf[(i + 1) % D], active, tbase, lane_base, nxt);
-      else tile_lookups<FMT, true>(buf[(i + 1) % D], active, tbase, lane_base, nxt);
-      tile_store<FMT, CH>(cur, t < tb, lane, col, b, t, n, y);
+      load_next(buf[(i + D - 1) % D]);
+      tile_lookups<FMT>(buf[(i + 1) % D], tbase, lane_base, nxt);
+      const uint32_t sw_nxt = active ? buf[(i + 1) % D].sc : 0u;
+      tile_store<FMT, CH>(cur, sw_cur, t < tb, lane, col, b, t, n, y);
+      sw_cur = sw_nxt;
       t += stride;
     }
   }
@@ -401,10 +427,10 @@ __global__ __launch_bounds__(kMainThreads, 3) void gemv_main_kernel(
 
 int bp_for(int64_t b) { return b <= 1 ? 1 : b <= 2 ? 2 : b <= 4 ? 4 : 8; }
 
-// table images (sub-slices of CH chunks) for this k and batch
-int64_t nsub_for(int64_t k, int ch) {
+// slices (2 CH chunks, two 64 KB table images each) for this k and batch
+int64_t nslices_for(int64_t k, int ch) {
   const int64_t chunks = k / kChunk;
-  return (chunks + ch - 1) / ch;
+  return (chunks + 2 * ch - 1) / (2 * ch);
 }
 
 // compute units of the current device (cached per device id)
@@ -424,10 +450,10 @@ int cu_count() {
 template <int FMT>
 hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
                        const uint16_t* scales, const float* lut, float* y, int64_t n, int64_t k,
-                       int b, int64_t ntiles, int64_t nsub, int64_t nslices) {
+                       int b, int64_t ntiles, int64_t nslices) {
 #define LOWBIT_LAUNCH(CHV)                                                                      \
   hipLaunchKernelGGL((gemv_main_kernel<FMT, CHV>), grid, dim3(kMainThreads), 0, st, codes,     \
-                     scales, lut, y, n, k, b, ntiles, nsub, nslices)
+                     scales, lut, y, n, k, b, ntiles, nslices)
   switch (ch) {
     case 64: LOWBIT_LAUNCH(64); break;
     case 32: LOWBIT_LAUNCH(32); break;
@@ -442,17 +468,17 @@ hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
 
 size_t gemv_workspace_bytes(int64_t k, int64_t b) {
   const int ch = kLanes / bp_for(b);
-  return (size_t)nsub_for(k, ch) * kSliceFloats * sizeof(float);
+  return (size_t)nslices_for(k, ch) * kImages * kSliceFloats * sizeof(float);
 }
 
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st) {
   const int ch = kLanes / bp_for(b);
-  const int64_t nsub = nsub_for(k, ch);
-  const int64_t build_threads = nsub * 16 * kLanes;
+  const int64_t nimages = nslices_for(k, ch) * kImages;
+  const int64_t build_threads = nimages * 16 * kLanes;
   const int64_t build_blocks = (build_threads + kWG - 1) / kWG;
   hipLaunchKernelGGL(gemv_build_kernel, dim3((unsigned)build_blocks), dim3(kWG), 0, st, x, k,
-                     (int)b, ch, nsub, static_cast<float*>(ws), y, n * b);
+                     (int)b, ch, nimages, static_cast<float*>(ws), y, n * b);
   return hipGetLastError();
 }
 
@@ -460,8 +486,7 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st) {
   const int ch = kLanes / bp_for(b);
-  const int64_t nsub = nsub_for(k, ch);
-  const int64_t nslices = (nsub + kCpl - 1) / kCpl;
+  const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
   const float* lut = static_cast<const float*>(ws);
   // G work-groups per slice: about one per CU in all, and no more than there
@@ -473,8 +498,8 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
   const int64_t nwg = G * nslices;
   dim3 grid((unsigned)nwg);
   if (fmt == 1)
-    return launch_main<1>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, nsub, nslices);
-  return launch_main<2>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, nsub, nslices);
+    return launch_main<1>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, nslices);
+  return launch_main<2>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, nslices);
 }
 
 }  // namespace lowbit

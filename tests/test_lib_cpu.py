@@ -73,11 +73,11 @@ def test_size_queries(lib):
 
 
 def test_workspace_query(lib):
-    # one 64 KB table image per K-slice; a slice is 512/BP weights of K
+    # two 64 KB table images per K-slice; a slice is 1024/BP weights of K
     for b, bp in [(1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)]:
-        k = 5120
-        slices = math.ceil((k // 8) / (64 // bp))
-        assert lowbit.lowbit_gemv_workspace_bytes("t2", 151936, k, b) == slices * 65536
+        for k in (128, 5120, 17408):
+            slices = math.ceil((k // 8) / (2 * (64 // bp)))
+            assert lowbit.lowbit_gemv_workspace_bytes("t2", 151936, k, b) == slices * 2 * 65536
     assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, 128, 0) == 0
     assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, 128, 9) == 0
 
