@@ -26,6 +26,14 @@ hipError_t launch_pack_t2(const int8_t* t, const uint16_t* s, int64_t n, int64_t
 hipError_t launch_unpack(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                          int64_t k, uint16_t* w, hipStream_t st);
 
+// decode GEMV: subset-sum tables for b < kMfmaMinBatch, matrix cores above
+constexpr int kMfmaMinBatch = 3;
+int64_t gemv_mfma_workspace_bytes(int64_t k);
+hipError_t launch_gemv_mfma_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
+                                    void* ws, hipStream_t st);
+hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                            int64_t k, int64_t b, float* y, const void* ws, int cus,
+                            hipStream_t st);
 size_t gemv_workspace_bytes(int64_t k, int64_t b);
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st);

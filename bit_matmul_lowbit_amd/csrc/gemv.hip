@@ -467,12 +467,14 @@ hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
 }  // namespace
 
 size_t gemv_workspace_bytes(int64_t k, int64_t b) {
+  if (b >= kMfmaMinBatch) return (size_t)gemv_mfma_workspace_bytes(k);
   const int ch = kLanes / bp_for(b);
   return (size_t)nslices_for(k, ch) * kImages * kSliceFloats * sizeof(float);
 }
 
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st) {
+  if (b >= kMfmaMinBatch) return launch_gemv_mfma_prepare(n, k, x, b, y, ws, st);
   const int ch = kLanes / bp_for(b);
   const int64_t nimages = nslices_for(k, ch) * kImages;
   const int64_t build_threads = nimages * 16 * kLanes;
@@ -485,6 +487,8 @@ hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t 
 hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t* scales,
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st) {
+  if (b >= kMfmaMinBatch)
+    return launch_gemv_mfma(fmt, codes, scales, n, k, b, y, ws, cu_count(), st);
   const int ch = kLanes / bp_for(b);
   const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;

@@ -73,11 +73,15 @@ def test_size_queries(lib):
 
 
 def test_workspace_query(lib):
-    # two 64 KB table images per K-slice; a slice is 1024/BP weights of K
-    for b, bp in [(1, 1), (2, 2), (3, 4), (4, 4), (5, 8), (8, 8)]:
+    # b = 1, 2: two 64 KB table images per K-slice of 1024 / b weights
+    for b in (1, 2):
         for k in (128, 5120, 17408):
-            slices = math.ceil((k // 8) / (2 * (64 // bp)))
+            slices = math.ceil((k // 8) / (128 // b))
             assert lowbit.lowbit_gemv_workspace_bytes("t2", 151936, k, b) == slices * 2 * 65536
+    # b >= 3 (matrix cores): x staged as MFMA operands, 4 KB per 128-weight group
+    for b in (3, 4, 5, 8):
+        for k in (128, 5120, 17408):
+            assert lowbit.lowbit_gemv_workspace_bytes("q1", 2048, k, b) == (k // 128) * 4096
     assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, 128, 0) == 0
     assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, 128, 9) == 0
 
