@@ -27,6 +27,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;
 constexpr int kThreads = 256;
@@ -35,28 +36,55 @@ constexpr int kRowU4 = BK / 8;  // 16-byte slots per LDS row
 // LDS uint4 index of 16-byte slot c of row r (XOR swizzle)
 __device__ __forceinline__ int slot(int r, int c) { return r * kRowU4 + (c ^ (r & 15)); }
 
-// 8 Q1 bits (LSB = first k) -> 8 BF16 values +1 (bit 1) / -1 (bit 0)
-__device__ __forceinline__ uint4 expand_q1(uint32_t b) {
-  const uint32_t nb = ~b;
-  uint32_t d[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    d[q] = 0x3F803F80u | (((nb >> (2 * q)) & 1u) << 15) | (((nb >> (2 * q + 1)) & 1u) << 31);
-  return make_uint4(d[0], d[1], d[2], d[3]);
+// Code byte -> 8 BF16 values, two per dword (k = 2p in the low half, 2p + 1
+// in the high half).  The byte is placed in the low byte of both 16-bit
+// halves; a packed 16-bit shift by (15 - 2p, 14 - 2p) brings bits 2p and
+// 2p + 1 to bits 15 and 31, where v_bitop3 uses them as sign bits (+1 and
+// -1 differ only there); ternary also masks the pairs whose pos xor neg bit
+// is clear.  Two (Q1) or five (T2) VALU operations per dword.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_shl(uint32_t d, uint32_t sh) {
+  const s16x2 a = __builtin_bit_cast(s16x2, d), s = __builtin_bit_cast(s16x2, sh);
+  return __builtin_bit_cast(uint32_t, (s16x2)(a << s));
 }
 
-// pos / neg bytes -> 8 BF16 values t = pos - neg in {-1, 0, +1}
-__device__ __forceinline__ uint4 expand_t2(uint32_t p, uint32_t q) {
-  const uint32_t nz = p ^ q;   // exactly one of pos / neg set
-  const uint32_t ng = q & ~p;  // t = -1
-  uint32_t d[4];
+__device__ __forceinline__ uint32_t pk_mask15(uint32_t d) {
+  const s16x2 a = __builtin_bit_cast(s16x2, d);
+  return __builtin_bit_cast(uint32_t, (s16x2)(a >> (s16x2){15, 15}));
+}
+
+// byte J of w in the low byte of both halves
+template <int J>
+__device__ __forceinline__ uint32_t rep_byte(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x0C000C00u | ((uint32_t)J << 16) | (uint32_t)J);
+}
+
+template <int P>
+constexpr uint32_t kPairShift = ((uint32_t)(14 - 2 * P) << 16) | (uint32_t)(15 - 2 * P);
+constexpr uint32_t kSignBits = 0x80008000u;
+constexpr uint32_t kOnes = 0x3F803F80u;  // BF16 +1 in both halves
+
+// Q1: bit 1 -> +1, bit 0 -> -1
+__device__ __forceinline__ uint4 expand_q1(uint32_t d) {
+  uint32_t v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = ((nz >> (2 * i)) & 1u) * 0x3F80u | (((ng >> (2 * i)) & 1u) << 15);
-    const uint32_t hi = ((nz >> (2 * i + 1)) & 1u) * 0x3F80u | (((ng >> (2 * i + 1)) & 1u) << 15);
-    d[i] = lo | (hi << 16);
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t sh = p == 0 ? kPairShift<0> : p == 1 ? kPairShift<1> : p == 2 ? kPairShift<2> : kPairShift<3>;
+    v[p] = kOnes | (~pk_shl(d, sh) & kSignBits);
   }
-  return make_uint4(d[0], d[1], d[2], d[3]);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ternary: dn = pos xor neg, dq = neg  ->  +1, -1 or 0 (0 also when both set)
+__device__ __forceinline__ uint4 expand_t2(uint32_t dn, uint32_t dq) {
+  uint32_t v[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t sh = p == 0 ? kPairShift<0> : p == 1 ? kPairShift<1> : p == 2 ? kPairShift<2> : kPairShift<3>;
+    v[p] = (kOnes | (pk_shl(dq, sh) & kSignBits)) & pk_mask15(pk_shl(dn, sh));
+  }
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -132,13 +160,13 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
   // tiles / columns load from valid addresses and are zeroed at use.
   constexpr int CW = (RPT * 1 + 3) / 4;  // code words per plane per thread
   struct Stage {
-    uint4 xr[XL];
+    u32x4 xr[XL];
     uint32_t p[CW], q[CW];
-    uint16_t sh[WBN];
+    uint32_t sh[WBN];
   };
-  auto fetch = [&](int64_t g, Stage& st) {
+  auto fetch = [&](int64_t g, Stage& st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) st.xr[j] = *reinterpret_cast<const uint4*>(xsrc[j] + g * BK);
+    for (int j = 0; j < XL; ++j) st.xr[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + g * BK);
     const uint8_t* cell = wsrc + g * kChunksPerGroup * CB;
     if constexpr (RPT == 8) {
       const uint2 a = *reinterpret_cast<const uint2*>(cell);
@@ -156,20 +184,41 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
 #pragma unroll
     for (int bj = 0; bj < WBN; ++bj) st.sh[bj] = sptr[bj][g * kTileRows];
   };
-  auto stash = [&](const Stage& st, int b) {
+  auto stash = [&](const Stage& st, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) xs[b][xdst[j]] = st.xr[j];
+    for (int j = 0; j < XL; ++j) xs[b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
-      const uint32_t pb = wvalid ? (st.p[rr >> 2] >> ((rr & 3) * 8)) & 0xFFu : 0u;
+      // codes of a tile past the end are replaced by zeros (Q1: -1, never
+      // stored; T2: 0)
+      const uint32_t pw = wvalid ? st.p[rr >> 2] : 0u;
+      uint32_t dp;
+      switch (rr & 3) {
+        case 0: dp = rep_byte<0>(pw); break;
+        case 1: dp = rep_byte<1>(pw); break;
+        case 2: dp = rep_byte<2>(pw); break;
+        default: dp = rep_byte<3>(pw); break;
+      }
       uint4 e;
-      if constexpr (FMT == 1) e = expand_q1(pb);
-      else e = expand_t2(pb, wvalid ? (st.q[rr >> 2] >> ((rr & 3) * 8)) & 0xFFu : 0u);
+      if constexpr (FMT == 1) {
+        e = expand_q1(dp);
+      } else {
+        const uint32_t qw = wvalid ? st.q[rr >> 2] : 0u;
+        uint32_t dq, dn;
+        switch (rr & 3) {
+          case 0: dq = rep_byte<0>(qw); dn = rep_byte<0>(pw ^ qw); break;
+          case 1: dq = rep_byte<1>(qw); dn = rep_byte<1>(pw ^ qw); break;
+          case 2: dq = rep_byte<2>(qw); dn = rep_byte<2>(pw ^ qw); break;
+          default: dq = rep_byte<3>(qw); dn = rep_byte<3>(pw ^ qw); break;
+        }
+        (void)dp;
+        e = expand_t2(dn, dq);
+      }
       ws[b][wdst[rr]] = e;
     }
   };
-  auto scale_of = [&](const Stage& st, int bj) {
-    return nvalid[bj] ? (float)__builtin_bit_cast(_Float16, st.sh[bj]) : 0.0f;
+  auto scale_of = [&](const Stage& st, int bj) __attribute__((always_inline)) {
+    return nvalid[bj] ? (float)__builtin_bit_cast(_Float16, (uint16_t)st.sh[bj]) : 0.0f;
   };
 
   f32x16 acc[WBM][WBN];
@@ -180,61 +229,82 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
 
-  // prologue: group 0 into LDS buffer 0
-  Stage cur, nxt;
-  fetch(0, cur);
-  stash(cur, 0);
+  // Ring of four register stages: group g + 3 is fetched while group g is
+  // multiplied and group g + 1 (fetched two iterations ago) is written to the
+  // other LDS buffer, so three groups of loads are in flight.  The stages are
+  // separate variables and the loop body is written out four times, so no
+  // stage is ever indexed at run time.
+  Stage s0, s1, s2, s3;
+  fetch(0, s0);
+  fetch(1 < groups ? 1 : groups - 1, s1);
+  fetch(2 < groups ? 2 : groups - 1, s2);
+  stash(s0, 0);
   float sv[WBN];
 #pragma unroll
-  for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(cur, bj);
+  for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(s0, bj);
   __syncthreads();
 
   const int kh = lane >> 5;  // which 8 of the 16 k of a step this lane holds
-  for (int64_t g = 0; g < groups; ++g) {
-    const int b = (int)(g & 1);
-    // next group's data (the last iteration re-fetches the last group into
-    // a buffer nobody reads, which keeps the loop body branch-free); the
-    // scheduling barrier keeps these loads at the top of the iteration
-    fetch(g + 1 < groups ? g + 1 : g, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-
-    f32x16 cg[WBM][WBN];
-#pragma unroll
-    for (int step = 0; step < BK / 16; ++step) {
-      bf16x8 a[WBM], bb[WBN];
-#pragma unroll
-      for (int bi = 0; bi < WBM; ++bi)
-        a[bi] = __builtin_bit_cast(bf16x8, xs[b][slot(wm * (BM / 2) + bi * 32 + jl, step * 2 + kh)]);
-#pragma unroll
-      for (int bj = 0; bj < WBN; ++bj)
-        bb[bj] = __builtin_bit_cast(bf16x8, ws[b][slot(wn * (BN / 2) + bj * 32 + jl, step * 2 + kh)]);
-#pragma unroll
-      for (int bi = 0; bi < WBM; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < WBN; ++bj) {
-          if (step == 0) {
-            const f32x16 zero = {};
-            cg[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], bb[bj], zero, 0, 0, 0);
-          } else {
-            cg[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], bb[bj], cg[bi][bj], 0, 0, 0);
-          }
-        }
-    }
-    // stage the next group into the other buffer (last read one iteration
-    // ago, before the barrier) while the matrix cores drain; the scheduling
-    // barrier keeps this work (which waits for the prefetch) below the MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    stash(nxt, b ^ 1);
-#pragma unroll
-    for (int bi = 0; bi < WBM; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < WBN; ++bj)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[bi][bj][v] = __builtin_fmaf(sv[bj], cg[bi][bj][v], acc[bi][bj][v]);
-#pragma unroll
-    for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(nxt, bj);
-    __syncthreads();
+  constexpr int RS = WBM * WBN >= 4 ? 2 : 8;  // k-steps whose operands are read at once
+  // one group: fetch group G + 3 into FAR, multiply group G from LDS buffer
+  // B, then stage group G + 1 (NEAR) into buffer B ^ 1.  Written as a macro
+  // so that the stages stay plain register variables.
+#define LOWBIT_GEMM_ITER(G, B, FAR, NEAR)                                                      \
+  {                                                                                           \
+    /* clamped: the tail re-fetches the last group into a stage nobody reads; */              \
+    /* the scheduling barrier keeps these loads at the top */                                 \
+    fetch((G) + 3 < groups ? (G) + 3 : groups - 1, FAR);                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    f32x16 cg[WBM][WBN];                                                                      \
+    /* operands of RS k-steps are read from LDS before their MFMAs, so one LDS */            \
+    /* round trip covers RS steps instead of one */                                           \
+    _Pragma("unroll") for (int s0 = 0; s0 < BK / 16; s0 += RS) {                              \
+      bf16x8 a[RS][WBM], bb[RS][WBN];                                                         \
+      _Pragma("unroll") for (int r = 0; r < RS; ++r) {                                        \
+        _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = __builtin_bit_cast(     \
+            bf16x8, xs[B][slot(wm * (BM / 2) + bi * 32 + jl, (s0 + r) * 2 + kh)]);            \
+        _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = __builtin_bit_cast(    \
+            bf16x8, ws[B][slot(wn * (BN / 2) + bj * 32 + jl, (s0 + r) * 2 + kh)]);            \
+      }                                                                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                      \
+      _Pragma("unroll") for (int r = 0; r < RS; ++r)                                          \
+      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi)                                      \
+      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) {                                    \
+        if (s0 + r == 0) {                                                                    \
+          const f32x16 zero = {};                                                             \
+          cg[bi][bj] =                                                                        \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][bi], bb[r][bj], zero, 0, 0, 0);    \
+        } else {                                                                              \
+          cg[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][bi], bb[r][bj],           \
+                                                               cg[bi][bj], 0, 0, 0);          \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    /* stage group G + 1 into the other buffer (last read one iteration ago, */              \
+    /* before the barrier) while the matrix cores drain */                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    stash(NEAR, (B) ^ 1);                                                                     \
+    /* a group past the end (the last block of four) leaves acc unchanged */                 \
+    const bool live = (G) < groups;                                                           \
+    _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi)                                        \
+    _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj)                                        \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                          \
+      const float f = __builtin_fmaf(sv[bj], cg[bi][bj][v], acc[bi][bj][v]);                  \
+      acc[bi][bj][v] = live ? f : acc[bi][bj][v];                                             \
+    }                                                                                         \
+    _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
+    __syncthreads();                                                                          \
   }
+  // Branch-free body (a branch would let the compiler sink the prefetch
+  // loads into the blocks that consume them); groups past the end run as
+  // no-ops.
+  for (int64_t g = 0; g < groups; g += 4) {
+    LOWBIT_GEMM_ITER(g, 0, s3, s1)
+    LOWBIT_GEMM_ITER(g + 1, 1, s0, s2)
+    LOWBIT_GEMM_ITER(g + 2, 0, s1, s3)
+    LOWBIT_GEMM_ITER(g + 3, 1, s2, s0)
+  }
+#undef LOWBIT_GEMM_ITER
 
   // epilogue: C[i][j] of a 32x32 block sits in lane j + 32*((i/4)%2), register
   // (i%4) + 4*(i/8)
