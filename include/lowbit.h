@@ -156,19 +156,21 @@ int lowbit_unpack(int fmt, const void* codes, const uint16_t* scales,
 /* Workspace bytes lowbit_gemv needs for (fmt, n, k, b); 0 on a bad shape. */
 size_t lowbit_gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b);
 
-/* GEMV phase 1: from x alone, build the subset-sum tables that
- * lowbit_gemv_accumulate reads, and set y to zero.
+/* GEMV phase 1: from x alone, prepare what lowbit_gemv_accumulate reads, and
+ * set y to zero.  For b <= 2 that is the subset-sum tables of x (one table
+ * entry per signed sum of 8 activations); for b >= 3 it is x laid out as
+ * matrix-core operands (batch rows padded to 16 with zeros).
  *   x_fp16    : [b][k] row-major FP16 activations (device, read-only)
  *   y_f32     : [b][n] row-major FP32 (device, written with zeros)
  *   workspace : at least lowbit_gemv_workspace_bytes(fmt, n, k, b) bytes
- *               (device, written; the tables do not depend on fmt).
+ *               (device, written; its contents do not depend on fmt).
  * Several matrices that share x and k (e.g. gate and up projections) may be
  * accumulated from one prepared workspace. */
 int lowbit_gemv_prepare(int64_t n, int64_t k, const uint16_t* x_fp16, int64_t b,
                         float* y_f32, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
-/* GEMV phase 2: y += W.x using the tables lowbit_gemv_prepare left in the
+/* GEMV phase 2: y += W.x using what lowbit_gemv_prepare left in the
  * workspace (same k and b).  This is the kernel that streams the weights.
  * Different K-slices of a row are added to y with FP32 atomic adds. */
 int lowbit_gemv_accumulate(int fmt, const void* codes, const uint16_t* scales,
