@@ -15,11 +15,12 @@
 // applied once per output).  The group scale multiplies the per-group sum.
 //
 // Data flow per call:
-//   1. build kernel (lowbit_gemv_prepare): every table S into the workspace,
-//      laid out exactly as the LDS image the main kernel copies; zeroes y.
+//   1. prepare kernel (lowbit_gemv_prepare): copies x into the workspace and
+//      zeroes y.
 //   2. main kernel (lowbit_gemv_accumulate): a work-group holds one K-slice:
 //      each lane owns two adjacent chunks of one group (two 64 KB tables,
-//      128 KB of LDS), and eight neighbouring lanes cover one group.  Per
+//      128 KB of LDS), and eight neighbouring lanes cover one group.  The
+//      work-group computes its slice's tables straight into LDS from x.  Per
 //      16-row tile a lane loads its 32 B (Q1) / 64 B (T2) of codes and one
 //      dword of scales; each code byte becomes one LDS lookup at
 //      (byte << 8) | (lane << 2) | (table << 16) -- a single v_perm_b32; every
@@ -74,42 +75,15 @@ __device__ __forceinline__ int64_t lane_chunk(int64_t s, int lanec, int ch, int 
   return s * 2 * ch + 16 * (lanec >> 3) + 2 * (lanec & 7) + q;
 }
 
-// build: table images, one thread per (image = slice*2 + q, hi nibble, lane)
-
-__global__ __launch_bounds__(kWG) void gemv_build_kernel(const uint16_t* __restrict__ x, int64_t k,
-                                                         int b, int ch, int64_t nimages,
-                                                         float* __restrict__ lut,
-                                                         float* __restrict__ y, int64_t ycount) {
+// prepare: x [b][k] -> workspace (read by the main kernel's table build), y = 0
+__global__ __launch_bounds__(kWG) void gemv_prepare_kernel(const uint4* __restrict__ x,
+                                                           int64_t nvec, uint4* __restrict__ xs,
+                                                           float* __restrict__ y,
+                                                           int64_t ycount) {
   const int64_t gid = (int64_t)blockIdx.x * kWG + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kWG;
   for (int64_t i = gid; i < ycount; i += stride) y[i] = 0.0f;
-  if (gid >= nimages * 16 * kLanes) return;
-  const int lane = (int)(gid & 63);
-  const int hi = (int)((gid >> 6) & 15);
-  const int64_t img = gid >> 10;
-  const int col = lane / ch;
-  const int64_t chunk = lane_chunk(img >> 1, lane % ch, ch, (int)(img & 1));
-  float* dst = lut + (img * kEntries + hi * 16) * kLanes + lane;
-  if (col >= b || chunk >= k / kChunk) {
-#pragma unroll
-    for (int lo = 0; lo < 16; ++lo) dst[lo * kLanes] = 0.0f;
-    return;
-  }
-  const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)col * k + chunk * kChunk);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float xv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) xv[j] = h2f((w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu);
-  float h = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) h += ((hi >> j) & 1) ? xv[4 + j] : -xv[4 + j];
-#pragma unroll
-  for (int lo = 0; lo < 16; ++lo) {
-    float a = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a += ((lo >> j) & 1) ? xv[j] : -xv[j];
-    dst[lo * kLanes] = a + h;
-  }
+  for (int64_t i = gid; i < nvec; i += stride) xs[i] = x[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -333,7 +307,7 @@ __device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, bool l
 template <int FMT, int CH>
 __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const float* __restrict__ lut, float* __restrict__ y, int64_t n, int64_t k, int b,
+    const uint16_t* __restrict__ xs, float* __restrict__ y, int64_t n, int64_t k, int b,
     int64_t ntiles, int64_t nslices) {
   __shared__ float4 table[kImages * kSliceFloats / 4];
   const int64_t s = blockIdx.x % nslices;
@@ -378,17 +352,23 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
     sn += sstep;
   };
 
-  // The slice's two table images (the build kernel zero-fills lanes without
-  // a chunk, so every entry read is finite) are loaded into registers first
-  // and written to LDS after the first tiles' loads are issued: loads
-  // complete in issue order, so the tables are not queued behind the tiles.
-  constexpr int kTableVecs = kImages * kSliceFloats / 4 / kMainThreads;
-  uint4 tv[kTableVecs];
+  // Table build, part 1: thread (image q, hi-nibble pair, lane L) loads the
+  // 8 activations of its chunk (zeros for a lane without a chunk: a column
+  // beyond b or a chunk past the end of K, so its entries are 0).  The load
+  // goes out before the first tiles' loads, which complete after it.
+  const int bl = threadIdx.x & 63;        // lane whose table column is built
+  const int bq = (threadIdx.x >> 9) & 1;  // image
+  const int bp = (threadIdx.x >> 6) & 7;  // hi nibbles 2 bp, 2 bp + 1
+  uint4 xv4;
   {
-    const __amdgpu_buffer_rsrc_t lr = tile_rsrc(reinterpret_cast<const uint8_t*>(lut + s * kImages * kSliceFloats),
-                                                kImages * kSliceFloats * 4);
-#pragma unroll
-    for (int i = 0; i < kTableVecs; ++i) tv[i] = bload<0>(lr, (threadIdx.x + i * kMainThreads) * 16u);
+    const int bcol = bl / CH;
+    const int64_t bchunk = lane_chunk(s, bl % CH, CH, bq);
+    const bool bvalid = bcol < b && bchunk < k / kChunk;
+    const __amdgpu_buffer_rsrc_t xr =
+        tile_rsrc(reinterpret_cast<const uint8_t*>(xs), (int64_t)b * k * 2);
+    // an offset past the resource returns zeros
+    const uint32_t xoff = bvalid ? (uint32_t)((bcol * k + bchunk * kChunk) * 2) : 0xFFFFFFF0u;
+    xv4 = bload<0>(xr, xoff);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -399,9 +379,35 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) load_next(buf[i]);
   __builtin_amdgcn_sched_barrier(0);
+
+  // Table build, part 2: S[e] = sum_j (bit j of e ? +x_j : -x_j) for the 32
+  // entries e = 16 hi + lo of this thread (hi = 2 bp, 2 bp + 1); entry e of
+  // lane L of image q sits at float q * 16384 + e * 64 + L, so a wave writes
+  // 64 consecutive floats per entry.
+  {
+    const uint32_t w4[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
+    float xv[8];
 #pragma unroll
-  for (int i = 0; i < kTableVecs; ++i)
-    table[threadIdx.x + i * kMainThreads] = __builtin_bit_cast(float4, tv[i]);
+    for (int j = 0; j < 8; ++j) xv[j] = h2f((w4[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu);
+    float lo_sum[16];
+#pragma unroll
+    for (int lo = 0; lo < 16; ++lo) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a += ((lo >> j) & 1) ? xv[j] : -xv[j];
+      lo_sum[lo] = a;
+    }
+    float* tabf = reinterpret_cast<float*>(table) + bq * kSliceFloats + bl;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int hi = 2 * bp + hh;
+      float h = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h += ((hi >> j) & 1) ? xv[4 + j] : -xv[4 + j];
+#pragma unroll
+      for (int lo = 0; lo < 16; ++lo) tabf[(hi * 16 + lo) * kLanes] = lo_sum[lo] + h;
+    }
+  }
   __syncthreads();
 
   // software pipeline: the lookups of the next tile are issued next to the
@@ -449,11 +455,11 @@ int cu_count() {
 
 template <int FMT>
 hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
-                       const uint16_t* scales, const float* lut, float* y, int64_t n, int64_t k,
+                       const uint16_t* scales, const uint16_t* xs, float* y, int64_t n, int64_t k,
                        int b, int64_t ntiles, int64_t nslices) {
 #define LOWBIT_LAUNCH(CHV)                                                                      \
   hipLaunchKernelGGL((gemv_main_kernel<FMT, CHV>), grid, dim3(kMainThreads), 0, st, codes,     \
-                     scales, lut, y, n, k, b, ntiles, nslices)
+                     scales, xs, y, n, k, b, ntiles, nslices)
   switch (ch) {
     case 64: LOWBIT_LAUNCH(64); break;
     case 32: LOWBIT_LAUNCH(32); break;
@@ -468,19 +474,18 @@ hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
 
 size_t gemv_workspace_bytes(int64_t k, int64_t b) {
   if (b >= kMfmaMinBatch) return (size_t)gemv_mfma_workspace_bytes(k);
-  const int ch = kLanes / bp_for(b);
-  return (size_t)nslices_for(k, ch) * kImages * kSliceFloats * sizeof(float);
+  return (size_t)(b * k * 2);  // x, from which the main kernel builds its tables
 }
 
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st) {
   if (b >= kMfmaMinBatch) return launch_gemv_mfma_prepare(n, k, x, b, y, ws, st);
-  const int ch = kLanes / bp_for(b);
-  const int64_t nimages = nslices_for(k, ch) * kImages;
-  const int64_t build_threads = nimages * 16 * kLanes;
-  const int64_t build_blocks = (build_threads + kWG - 1) / kWG;
-  hipLaunchKernelGGL(gemv_build_kernel, dim3((unsigned)build_blocks), dim3(kWG), 0, st, x, k,
-                     (int)b, ch, nimages, static_cast<float*>(ws), y, n * b);
+  const int64_t nvec = b * k / 8;  // 16-byte vectors of x (k % 128 == 0)
+  const int64_t work = nvec > n * b ? nvec : n * b;
+  int64_t blocks = (work + kWG - 1) / kWG;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(gemv_prepare_kernel, dim3((unsigned)blocks), dim3(kWG), 0, st,
+                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b);
   return hipGetLastError();
 }
 
@@ -492,7 +497,7 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
   const int ch = kLanes / bp_for(b);
   const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
-  const float* lut = static_cast<const float*>(ws);
+  const uint16_t* xs = static_cast<const uint16_t*>(ws);
   // G work-groups per slice: about one per CU in all, and no more than there
   // are 16-tile blocks
   int64_t G = (int64_t)cu_count() / nslices;
@@ -502,8 +507,8 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
   const int64_t nwg = G * nslices;
   dim3 grid((unsigned)nwg);
   if (fmt == 1)
-    return launch_main<1>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, nslices);
-  return launch_main<2>(ch, grid, st, codes, scales, lut, y, n, k, (int)b, ntiles, nslices);
+    return launch_main<1>(ch, grid, st, codes, scales, xs, y, n, k, (int)b, ntiles, nslices);
+  return launch_main<2>(ch, grid, st, codes, scales, xs, y, n, k, (int)b, ntiles, nslices);
 }
 
 }  // namespace lowbit
