@@ -4,7 +4,7 @@
 Default workload ``t2_lmhead_152k``: the ternary g128 LM-head decode GEMV,
 W 151936 x 5120 (2.125 bits per weight: 206,632,960 bytes of codes + scales),
 x FP16 [1][5120], y FP32.  One step = one full decode product: the table
-build from x (lowbit_gemv_prepare) and the weight-streaming accumulation
+preparation of x (lowbit_gemv_prepare) and the weight-streaming accumulation
 (lowbit_gemv_accumulate), on the next of R distinct device copies of the
 packed weights (R copies >= 1 GiB, four times the 256 MB last-level cache, so
 every step reads its weights from HBM).  Inputs are resident in HBM before the
@@ -18,7 +18,10 @@ Printed: one JSON line with
              rocprofv3 counters gave for the same kernel source, or null
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
   secondary  the other workloads: decode GEMVs (fused FFN shapes, batch
-             sweep), the FP16 -> Q1 quantiser and the pp512 prefill GEMMs
+             sweep), the FP16 -> Q1 quantiser and the pp512 prefill GEMMs;
+             for the GEMVs also the per-step time of a HIP graph that holds
+             one step per rotated copy (small matrices are otherwise timed
+             by the host's launch rate)
 ``--gpus N`` with N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -78,8 +81,10 @@ def rotated_copies(codes, scales):
 # ---------------------------------------------------------------------------
 # GEMV timing
 
-def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True):
-    """Returns dict with step GB/s, ms/step and the mean accumulate-kernel time."""
+def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_graph=False):
+    """Returns dict with step GB/s, ms/step and the mean accumulate-kernel time;
+    with_graph adds the per-step time of a HIP graph holding one step per
+    rotated copy (prepare + accumulate, no host work between launches)."""
     import torch
 
     from bit_matmul_lowbit_amd import lowbit, synth
@@ -127,12 +132,38 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True):
         torch.cuda.synchronize()
         kernel_ms = ev0.elapsed_time(ev1) / steps
 
+    graph_ms = None
+    if with_graph:
+        # one captured step per rotated copy (>= 1 GiB of weights, so still
+        # cold), replayed a few times; no host work sits between the launches
+        nc = len(copies)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(nc):
+                    c, s = copies[i]
+                    lowbit.lowbit_gemv_prepare(n, k, x, y, ws)
+                    lowbit.lowbit_gemv_accumulate(fmt, c, s, n, k, b, y, ws)
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 3
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) / (reps * nc) * 1e3
+        del g
+
     out = {
         "weight_bytes": wbytes,
         "copies": len(copies),
         "ms_per_step": elapsed / steps * 1e3,
         "gbs": wbytes * steps / elapsed / 1e9,
         "kernel_ms": kernel_ms,
+        "graph_ms_per_step": graph_ms,
     }
     del copies
     torch.cuda.empty_cache()
@@ -332,9 +363,11 @@ def main():
         }.items():
             for b2 in ([1, 2, 5, 8] if "27b" in name else [1]):
                 key = name if "27b" not in name else f"{name}_b{b2}"
-                rr = time_gemv(f2, n2, k2, b2, seeds, 50, 10)
+                rr = time_gemv(f2, n2, k2, b2, seeds, 50, 10, with_graph=True)
                 sec[key] = {"gbs": round(rr["gbs"], 1), "us_per_step": round(rr["ms_per_step"] * 1e3, 2),
-                            "kernel_gbs": round(rr["weight_bytes"] / (rr["kernel_ms"] * 1e-3) / 1e9, 1)}
+                            "kernel_gbs": round(rr["weight_bytes"] / (rr["kernel_ms"] * 1e-3) / 1e9, 1),
+                            "graph_us_per_step": round(rr["graph_ms_per_step"] * 1e3, 2),
+                            "graph_gbs": round(rr["weight_bytes"] / (rr["graph_ms_per_step"] * 1e-3) / 1e9, 1)}
                 log(f"[bench] {key}: {sec[key]}")
         q = time_quantize(151936, 5120, 1003, 20, 3)
         sec["q1_quantize_151936x5120"] = {"gbs": round(q["gbs"], 1), "us": round(q["ms"] * 1e3, 1),
