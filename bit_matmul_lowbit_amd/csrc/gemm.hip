@@ -94,8 +94,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <int FMT, bool OUT_F32, int BM, int BN>
-__global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm_kernel(
+// 64 x 64 tiles keep a single LDS buffer per team (3 waves per SIMD fit);
+// larger tiles double-buffer
+template <int BM, int BN>
+constexpr bool kSingleBuffer = BM * BN == 64 * 64;
+
+template <int FMT, bool OUT_F32, int BM, int BN, int KT>
+__global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) void gemm_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y) {
   constexpr int WBM = BM / 64;                    // 32-row blocks per wave
@@ -105,10 +110,15 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
   constexpr int RPT = BN / 16;                    // W rows expanded per thread per group
   constexpr int TPC = 16 / RPT;                   // threads per code cell
 
-  __shared__ uint4 xs[2][BM * kRowU4];
-  __shared__ uint4 ws[2][BN * kRowU4];
+  constexpr bool kSingle = kSingleBuffer<BM, BN>;
+  constexpr int NB = kSingle ? 1 : 2;  // LDS buffers per team
+  __shared__ uint4 xs[KT][NB][BM * kRowU4];
+  __shared__ uint4 ws[KT][NB][BN * kRowU4];
 
-  const int tid = threadIdx.x;
+  // KT teams of 256 threads share the output tile; team t takes the groups
+  // g = t (mod KT) and has its own LDS buffers
+  const int tid = threadIdx.x & (kThreads - 1);
+  const int team = KT == 1 ? 0 : (int)(threadIdx.x / kThreads);
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -131,9 +141,11 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
     xdst[j] = slot(i >> 4, i & 15);
   }
 
-  // --- W codes: thread -> cell ci = tid / TPC (row tile ci/16, chunk ci%16
-  // of the group), rows part*RPT .. part*RPT + RPT-1 of that cell
-  const int ci = tid / TPC, part = tid % TPC;
+  // --- W codes: thread -> cell ci = tid % BN (row tile ci/16, chunk ci%16
+  // of the group), rows part*RPT .. part*RPT + RPT-1 of that cell, part =
+  // tid / BN; eight consecutive lanes write one row, eight different slots
+  static_assert(kThreads / TPC == BN, "one thread per cell and part");
+  const int ci = tid % BN, part = tid / BN;
   const int wt = ci >> 4, wc = ci & 15;
   const int64_t gtile = n0 / kTileRows + wt;
   const bool wvalid = gtile < ntiles;
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
   };
   auto stash = [&](const Stage& st, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) xs[b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
+    for (int j = 0; j < XL; ++j) xs[team][b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       // codes of a tile past the end are replaced by zeros (Q1: -1, never
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
         (void)dp;
         e = expand_t2(dn, dq);
       }
-      ws[b][wdst[rr]] = e;
+      ws[team][b][wdst[rr]] = e;
     }
   };
   auto scale_of = [&](const Stage& st, int bj) __attribute__((always_inline)) {
@@ -229,23 +241,128 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
 
+  // local group index gl -> group gl * KT + team, clamped to the last group
+  // (fetched into a stage whose result is discarded)
+  const int64_t nloc = (groups + KT - 1) / KT;
+  auto gof = [&](int64_t gl) __attribute__((always_inline)) {
+    const int64_t g = gl * KT + team;
+    return g < groups ? g : groups - 1;
+  };
+  const int kh = lane >> 5;  // which 8 of the 16 k of a step this lane holds
+  // a single 32 x 32 block per wave runs two independent accumulation chains
+  // (even and odd k-steps), so consecutive MFMAs do not wait on each other
+  constexpr int NCH = (WBM * WBN == 1 && !kSingle) ? 2 : 1;
+  auto read_a = [&](int b, int step, int bi) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, xs[team][b][slot(wm * (BM / 2) + bi * 32 + jl, step * 2 + kh)]);
+  };
+  auto read_b = [&](int b, int step, int bj) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, ws[team][b][slot(wn * (BN / 2) + bj * 32 + jl, step * 2 + kh)]);
+  };
+  auto mfma_step = [&](f32x16 (&cg)[NCH][WBM][WBN], int step, const bf16x8 (&a)[WBM],
+                       const bf16x8 (&bb)[WBN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bi = 0; bi < WBM; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < WBN; ++bj) {
+        const int ch = step % NCH;
+        const f32x16 zero = {};
+        cg[ch][bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a[bi], bb[bj], step < NCH ? zero : cg[ch][bi][bj], 0, 0, 0);
+      }
+  };
+  // acc += s * (sum of the chains); a group past the end leaves acc unchanged
+  auto scale_add = [&](const f32x16 (&cg)[NCH][WBM][WBN], const float (&sv)[WBN], bool live)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int bi = 0; bi < WBM; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < WBN; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float f = __builtin_fmaf(sv[bj], cg[0][bi][bj][v], acc[bi][bj][v]);
+          if constexpr (NCH == 2) f = __builtin_fmaf(sv[bj], cg[NCH - 1][bi][bj][v], f);
+          acc[bi][bj][v] = live ? f : acc[bi][bj][v];
+        }
+  };
+
+  if constexpr (kSingle) {
+    // Ring of three register stages over ONE LDS buffer: group g + 2 is
+    // fetched while group g is multiplied.  The operands of g are read from
+    // LDS in two halves of four k-steps; once every wave holds the second
+    // half (barrier), group g + 1 is written over them while the last four
+    // k-steps run.  Stages are separate variables and the body is written out
+    // three times, so no stage is indexed at run time.
+    Stage s0, s1, s2;
+    fetch(gof(0), s0);
+    fetch(gof(1), s1);
+    stash(s0, 0);
+    float sv[WBN];
+#pragma unroll
+    for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(s0, bj);
+    __syncthreads();
+    constexpr int kValu = FMT == 1 ? 10 : 21;  // staging VALU per MFMA of the second half
+#define LOWBIT_GEMM_ITER1(G, FAR, NEAR)                                                        \
+  {                                                                                           \
+    fetch(gof((G) + 2), FAR);                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    f32x16 cg[NCH][WBM][WBN];                                                                 \
+    bf16x8 a[4][WBM], bb[4][WBN];                                                             \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                           \
+      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = read_a(0, r, bi);         \
+      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = read_b(0, r, bj);        \
+    }                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    /* steps 0..3, each followed by the reads of step r + 4 into its registers */            \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                           \
+      mfma_step(cg, r, a[r], bb[r]);                                                          \
+      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = read_a(0, r + 4, bi);     \
+      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = read_b(0, r + 4, bj);    \
+    }                                                                                         \
+    _Pragma("unroll") for (int r = 0; r < 4 * WBM * WBN; ++r) {                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, (WBM + WBN) / (WBM * WBN), 0);              \
+    }                                                                                         \
+    /* every wave holds its operands: the buffer may be overwritten */                       \
+    __syncthreads();                                                                          \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) mfma_step(cg, r + 4, a[r], bb[r]);          \
+    stash(NEAR, 0);                                                                           \
+    _Pragma("unroll") for (int r = 0; r < 4 * WBM * WBN; ++r) {                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                                  \
+      __builtin_amdgcn_sched_group_barrier(0x200, (XL + RPT) / 4, 0);                         \
+    }                                                                                         \
+    scale_add(cg, sv, (G) * KT + team < groups);                                              \
+    _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
+    __syncthreads();                                                                          \
+  }
+    // Branch-free body (a branch would let the compiler sink the prefetch
+    // loads into the blocks that consume them); groups past the end run as
+    // no-ops.
+    for (int64_t g = 0; g < nloc; g += 3) {
+      LOWBIT_GEMM_ITER1(g, s2, s1)
+      LOWBIT_GEMM_ITER1(g + 1, s0, s2)
+      LOWBIT_GEMM_ITER1(g + 2, s1, s0)
+    }
+#undef LOWBIT_GEMM_ITER1
+  } else {
   // Ring of four register stages: group g + 3 is fetched while group g is
   // multiplied and group g + 1 (fetched two iterations ago) is written to the
   // other LDS buffer, so three groups of loads are in flight.  The stages are
   // separate variables and the loop body is written out four times, so no
   // stage is ever indexed at run time.
   Stage s0, s1, s2, s3;
-  fetch(0, s0);
-  fetch(1 < groups ? 1 : groups - 1, s1);
-  fetch(2 < groups ? 2 : groups - 1, s2);
+  fetch(gof(0), s0);
+  fetch(gof(1), s1);
+  fetch(gof(2), s2);
   stash(s0, 0);
   float sv[WBN];
 #pragma unroll
   for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(s0, bj);
   __syncthreads();
 
-  const int kh = lane >> 5;  // which 8 of the 16 k of a step this lane holds
   constexpr int RS = WBM * WBN >= 4 ? 2 : 8;  // k-steps whose operands are read at once
+  constexpr bool kInterleave = RS == BK / 16;
+  constexpr int kValuPerMfma = FMT == 1 ? 4 : 8;
   // one group: fetch group G + 3 into FAR, multiply group G from LDS buffer
   // B, then stage group G + 1 (NEAR) into buffer B ^ 1.  Written as a macro
   // so that the stages stay plain register variables.
@@ -253,43 +370,53 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
   {                                                                                           \
     /* clamped: the tail re-fetches the last group into a stage nobody reads; */              \
     /* the scheduling barrier keeps these loads at the top */                                 \
-    fetch((G) + 3 < groups ? (G) + 3 : groups - 1, FAR);                                      \
+    fetch(gof((G) + 3), FAR);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                        \
-    f32x16 cg[WBM][WBN];                                                                      \
+    f32x16 cg[NCH][WBM][WBN];                                                                 \
     /* operands of RS k-steps are read from LDS before their MFMAs, so one LDS */            \
     /* round trip covers RS steps instead of one */                                           \
     _Pragma("unroll") for (int s0 = 0; s0 < BK / 16; s0 += RS) {                              \
       bf16x8 a[RS][WBM], bb[RS][WBN];                                                         \
       _Pragma("unroll") for (int r = 0; r < RS; ++r) {                                        \
         _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = __builtin_bit_cast(     \
-            bf16x8, xs[B][slot(wm * (BM / 2) + bi * 32 + jl, (s0 + r) * 2 + kh)]);            \
+            bf16x8, xs[team][B][slot(wm * (BM / 2) + bi * 32 + jl, (s0 + r) * 2 + kh)]);            \
         _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = __builtin_bit_cast(    \
-            bf16x8, ws[B][slot(wn * (BN / 2) + bj * 32 + jl, (s0 + r) * 2 + kh)]);            \
+            bf16x8, ws[team][B][slot(wn * (BN / 2) + bj * 32 + jl, (s0 + r) * 2 + kh)]);            \
       }                                                                                       \
       __builtin_amdgcn_sched_barrier(0);                                                      \
       _Pragma("unroll") for (int r = 0; r < RS; ++r)                                          \
       _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi)                                      \
       _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) {                                    \
-        if (s0 + r == 0) {                                                                    \
+        const int ch = (s0 + r) % NCH;                                                        \
+        if (s0 + r < NCH) {                                                                   \
           const f32x16 zero = {};                                                             \
-          cg[bi][bj] =                                                                        \
+          cg[ch][bi][bj] =                                                                    \
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][bi], bb[r][bj], zero, 0, 0, 0);    \
         } else {                                                                              \
-          cg[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][bi], bb[r][bj],           \
-                                                               cg[bi][bj], 0, 0, 0);          \
+          cg[ch][bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r][bi], bb[r][bj],       \
+                                                                   cg[ch][bi][bj], 0, 0, 0);  \
         }                                                                                     \
       }                                                                                       \
     }                                                                                         \
     /* stage group G + 1 into the other buffer (last read one iteration ago, */              \
-    /* before the barrier) while the matrix cores drain */                                    \
-    __builtin_amdgcn_sched_barrier(0);                                                        \
+    /* before the barrier) while the matrix cores work: when every operand */                \
+    /* was read up front, the staging is interleaved with the MFMAs */                       \
+    if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);                            \
     stash(NEAR, (B) ^ 1);                                                                     \
+    if constexpr (kInterleave) {                                                              \
+      _Pragma("unroll") for (int i = 0; i < WBM * WBN * (BK / 16); ++i) {                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    \
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);                         \
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                    \
+      }                                                                                       \
+    }                                                                                         \
     /* a group past the end (the last block of four) leaves acc unchanged */                 \
-    const bool live = (G) < groups;                                                           \
+    const bool live = (G) * KT + team < groups;                                               \
     _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi)                                        \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj)                                        \
     _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                          \
-      const float f = __builtin_fmaf(sv[bj], cg[bi][bj][v], acc[bi][bj][v]);                  \
+      float f = __builtin_fmaf(sv[bj], cg[0][bi][bj][v], acc[bi][bj][v]);                     \
+      if constexpr (NCH == 2) f = __builtin_fmaf(sv[bj], cg[NCH - 1][bi][bj][v], f);          \
       acc[bi][bj][v] = live ? f : acc[bi][bj][v];                                             \
     }                                                                                         \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
@@ -298,13 +425,40 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 128 * 128) ? 1 : 2) void gemm
   // Branch-free body (a branch would let the compiler sink the prefetch
   // loads into the blocks that consume them); groups past the end run as
   // no-ops.
-  for (int64_t g = 0; g < groups; g += 4) {
+  for (int64_t g = 0; g < nloc; g += 4) {
     LOWBIT_GEMM_ITER(g, 0, s3, s1)
     LOWBIT_GEMM_ITER(g + 1, 1, s0, s2)
     LOWBIT_GEMM_ITER(g + 2, 0, s1, s3)
     LOWBIT_GEMM_ITER(g + 3, 1, s2, s0)
   }
 #undef LOWBIT_GEMM_ITER
+  }
+
+  if constexpr (KT > 1) {
+    // teams 1.. leave their sums in their own (no longer read) LDS buffers;
+    // team 0 adds them and stores the tile
+    if (team > 0) {
+      float* red = reinterpret_cast<float*>(&xs[team][0][0]);
+#pragma unroll
+      for (int bi = 0; bi < WBM; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < WBN; ++bj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) red[((bi * WBN + bj) * 16 + v) * kThreads + tid] = acc[bi][bj][v];
+    }
+    __syncthreads();
+    if (team > 0) return;
+#pragma unroll
+    for (int t = 1; t < KT; ++t) {
+      const float* red = reinterpret_cast<const float*>(&xs[t][0][0]);
+#pragma unroll
+      for (int bi = 0; bi < WBM; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < WBN; ++bj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[bi][bj][v] += red[((bi * WBN + bj) * 16 + v) * kThreads + tid];
+    }
+  }
 
   // epilogue: C[i][j] of a 32x32 block sits in lane j + 32*((i/4)%2), register
   // (i%4) + 4*(i/8)
@@ -340,16 +494,16 @@ int cu_count_gemm() {
   return cached[dev];
 }
 
-template <int FMT, int BM, int BN>
+template <int FMT, int BM, int BN, int KT>
 hipError_t launch_tile(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                        const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
   const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
   if (out_f32)
-    hipLaunchKernelGGL((gemm_kernel<FMT, true, BM, BN>), grid, dim3(kThreads), 0, st, codes,
-                       scales, x, m, n, k, y);
+    hipLaunchKernelGGL((gemm_kernel<FMT, true, BM, BN, KT>), grid, dim3(kThreads * KT), 0, st,
+                       codes, scales, x, m, n, k, y);
   else
-    hipLaunchKernelGGL((gemm_kernel<FMT, false, BM, BN>), grid, dim3(kThreads), 0, st, codes,
-                       scales, x, m, n, k, y);
+    hipLaunchKernelGGL((gemm_kernel<FMT, false, BM, BN, KT>), grid, dim3(kThreads * KT), 0, st,
+                       codes, scales, x, m, n, k, y);
   return hipGetLastError();
 }
 
@@ -360,8 +514,13 @@ hipError_t launch_fmt(const uint8_t* codes, const uint16_t* scales, int64_t n, i
   // 64 x 64 tiles (4x as many work-groups)
   const int64_t big = ((n + 127) / 128) * ((m + 127) / 128);
   if (big >= 2 * (int64_t)cu_count_gemm())
-    return launch_tile<FMT, 128, 128>(codes, scales, n, k, x, m, y, out_f32, st);
-  return launch_tile<FMT, 64, 64>(codes, scales, n, k, x, m, y, out_f32, st);
+    return launch_tile<FMT, 128, 128, 1>(codes, scales, n, k, x, m, y, out_f32, st);
+  // with no more 64 x 64 tiles than CUs, two K-teams per tile (one 8-wave
+  // work-group per CU) keep twice as many waves busy
+  const int64_t small = ((n + 63) / 64) * ((m + 63) / 64);
+  if (small <= (int64_t)cu_count_gemm() && k >= 2 * BK)
+    return launch_tile<FMT, 64, 64, 2>(codes, scales, n, k, x, m, y, out_f32, st);
+  return launch_tile<FMT, 64, 64, 1>(codes, scales, n, k, x, m, y, out_f32, st);
 }
 
 }  // namespace

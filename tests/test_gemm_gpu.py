@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from bit_matmul_lowbit_amd import lowbit, synth
-from tests.helpers import assert_close, dev_u16, host_u16, host_u8, say
+from tests.helpers import TOL, assert_close, dev_u16, host_u16, host_u8, say
 
 pytestmark = pytest.mark.gpu
 
@@ -52,15 +52,24 @@ def _rne_f32_to_bf16(f32):
 
 
 def _bf16_ulp_ok(yb, ref64):
-    """|y - ref| <= one BF16 ulp at |ref| (the FP32 sum may sit on the other
-    side of a rounding boundary than the exact value)."""
+    """|y - ref| <= one BF16 ulp at |ref| + TOL * 0.01 * rms(row of ref).
+
+    y is the nearest-even rounding of the FP32 sum (checked bit for bit
+    separately), so |y - ref| <= ulp/2 + |FP32 sum - ref|; the FP32 error is
+    bounded by the floored tolerance, whose floor is 1% of the row's RMS.  For
+    ordinary outputs the ulp term dominates; outputs near zero by cancellation
+    (below the floor) get the FP32 bound, which a BF16 ulp there can be far
+    smaller than."""
     import torch
 
     y = torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     a = np.abs(ref64)
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     ulp = np.exp2(np.maximum(e, -126) - 7)
-    return np.all(np.abs(y - ref64) <= ulp * 1.0000001 + 1e-30)
+    r2 = np.atleast_2d(ref64)
+    rms = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True)).reshape(ref64.shape[:-1] + (1,)) \
+        if ref64.ndim else np.float64(0.0)
+    return np.all(np.abs(y - ref64) <= ulp * 1.0000001 + TOL * 0.01 * rms + 1e-30)
 
 
 SHAPES = [(1, 16, 128), (5, 37, 384), (64, 128, 256), (130, 200, 640), (256, 129, 1280), (300, 300, 2048)]
