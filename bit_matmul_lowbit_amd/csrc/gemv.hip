@@ -354,8 +354,10 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
 
   // Table build, part 1: thread (image q, hi-nibble pair, lane L) loads the
   // 8 activations of its chunk (zeros for a lane without a chunk: a column
-  // beyond b or a chunk past the end of K, so its entries are 0).  The load
-  // goes out before the first tiles' loads, which complete after it.
+  // beyond b or a chunk past the end of K, so its entries are 0).  The wave
+  // waits for it before any weight load goes out: behind a burst of weight
+  // loads from every CU, this small load took microseconds to return and
+  // held back the tables (and so every lookup).
   const int bl = threadIdx.x & 63;        // lane whose table column is built
   const int bq = (threadIdx.x >> 9) & 1;  // image
   const int bp = (threadIdx.x >> 6) & 7;  // hi nibbles 2 bp, 2 bp + 1
@@ -371,13 +373,15 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
     xv4 = bload<0>(xr, xoff);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // an empty statement that reads xv4: the compiler waits for the load here
+  __asm__ volatile("" ::"v"(xv4.x), "v"(xv4.y), "v"(xv4.z), "v"(xv4.w));
 
   // ring of D register sets: the loads of the next D-1 tiles of this wave
-  // are in flight while one tile is contracted
+  // are in flight while one tile is contracted.  The first goes out before
+  // the table build, the others after it.
   constexpr int D = kDepth<FMT, CH>;
   TileRegs<FMT> buf[D];
-#pragma unroll
-  for (int i = 0; i < D - 1; ++i) load_next(buf[i]);
+  load_next(buf[0]);
   __builtin_amdgcn_sched_barrier(0);
 
   // Table build, part 2: S[e] = sum_j (bit j of e ? +x_j : -x_j) for the 32
@@ -409,6 +413,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int i = 1; i < D - 1; ++i) load_next(buf[i]);
 
   // software pipeline: the lookups of the next tile are issued next to the
   // reduction of the current one, two independent dependency chains
