@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   // This work-group's items: blockIdx.x + i * gridDim.x.  Every wave runs
   // `per` group slots per item (slot i of an item is group
   // piece * gpp + wave + 4 i); a slot past the item's groups, or past the
-  // last item, is loaded with zero scales and zero x and adds exact zeros.
+  // last item, is loaded from a zero-length resource (codes, scales and x
+  // read as zeros, with no memory traffic) and adds exact zeros.
   const int per = (gpp + kWaves - 1) / kWaves;
   const int64_t nit = nitems > (int64_t)blockIdx.x
                           ? (nitems - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
     const __amdgpu_buffer_rsrc_t rc = rsrc(codes + T0 * cpitch, here * cpitch);
     const __amdgpu_buffer_rsrc_t rs =
         rsrc(reinterpret_cast<const uint8_t*>(scales) + T0 * spitch, here * spitch);
-    load_group<FMT>(r, rc, live ? rs : rz, live ? rx : rz, voff_c, voff_s, voff_x,
+    load_group<FMT>(r, live ? rc : rz, live ? rs : rz, live ? rx : rz, voff_c, voff_s, voff_x,
                     live ? g : 0);
   };
 
