@@ -157,8 +157,9 @@ int lowbit_unpack(int fmt, const void* codes, const uint16_t* scales,
 size_t lowbit_gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b);
 
 /* GEMV phase 1: from x alone, prepare what lowbit_gemv_accumulate reads, and
- * set y to zero.  For b <= 2 that is the subset-sum tables of x (one table
- * entry per signed sum of 8 activations); for b >= 3 it is x laid out as
+ * set y to zero.  For b <= 2 that is a copy of x (each work-group of the
+ * accumulate kernel builds its subset-sum tables -- one entry per signed
+ * sum of 8 activations -- from it in LDS); for b >= 3 it is x laid out as
  * matrix-core operands (batch rows padded to 16 with zeros).
  *   x_fp16    : [b][k] row-major FP16 activations (device, read-only)
  *   y_f32     : [b][n] row-major FP32 (device, written with zeros)
