@@ -79,6 +79,12 @@ def _load():
         lib.orc_gemv_rows.restype = None
         lib.orc_gemm_rows.argtypes = [ctypes.c_int, p, p, i64, i64, p, i64, i64, i64, i64, p, p]
         lib.orc_gemm_rows.restype = None
+        lib.orc_f64_to_fp16_rne.argtypes = [ctypes.c_double]
+        lib.orc_f64_to_fp16_rne.restype = ctypes.c_uint16
+        lib.orc_silu.argtypes = [ctypes.c_double]
+        lib.orc_silu.restype = ctypes.c_double
+        lib.orc_ffn_hidden.argtypes = [ctypes.c_int, p, p, i64, i64, p, i64, p, p, p]
+        lib.orc_ffn_hidden.restype = None
         _lib = lib
     return _lib
 
@@ -114,6 +120,22 @@ def f64_to_bf16_rne_array(v: np.ndarray) -> np.ndarray:
 
 # --------------------------------------------------------------------------
 # layout
+
+def f64_to_fp16_rne(v: float) -> int:
+    """double -> FP16 pattern, nearest-even (|v| >= 65520 -> infinity)."""
+    return int(_load().orc_f64_to_fp16_rne(float(v)))
+
+
+def f64_to_fp16_rne_array(v: np.ndarray) -> np.ndarray:
+    f = _load().orc_f64_to_fp16_rne
+    flat = np.asarray(v, dtype=np.float64).ravel()
+    return np.array([f(float(a)) for a in flat], dtype=np.uint16).reshape(np.shape(v))
+
+
+def silu(v: float) -> float:
+    """SiLU(v) = v / (1 + e^-v) in double."""
+    return float(_load().orc_silu(float(v)))
+
 
 def codes_bytes(fmt: int, n: int, k: int) -> int:
     return int(_load().orc_codes_bytes(fmt, n, k))
@@ -210,3 +232,38 @@ def gemm(fmt, codes, scales, n, k, x_bf16, m0=0, mrows=None, row0=0, nrows=None)
                           _ptr(np.ascontiguousarray(scales)), n, k, _ptr(x), m0, mrows,
                           row0, nrows, _ptr(xbuf), _ptr(y))
     return y
+
+
+# --------------------------------------------------------------------------
+# decode FFN (gated MLP of the Qwen-derived models the pages compress)
+#
+# [P2] "Como funciona la compresion" and [P4] "Configuracion multimodal y de
+# bajo bit de extremo a extremo": the MLP projections are low-bit like every
+# other matrix.  [P5] "Detalles tecnicos": decode kernels were tuned at the
+# matvec / FFN level.  The pages do not spell out the MLP; it is read as the
+# gated form of the Qwen family, y = W_dn (SiLU(W_gate x) * (W_up x)), with
+# gate and up stacked in one [2f][k] matrix (gate rows first) and the
+# elementwise product rounded to FP16, the activation type every GEMV of the
+# path reads.
+
+def ffn_hidden(fmt, gu_codes, gu_scales, k, f, x_fp16) -> np.ndarray:
+    """z[b][f] FP16 patterns: RNE_fp16(SiLU(h_gate) * h_up), h = W_gu x exact."""
+    x = np.ascontiguousarray(np.atleast_2d(x_fp16), dtype=np.uint16)
+    b = x.shape[0]
+    assert x.shape[1] == k
+    z = np.zeros((b, f), dtype=np.uint16)
+    xbuf = np.zeros(b * k, dtype=np.float64)
+    hbuf = np.zeros(b * 2 * f, dtype=np.float64)
+    _load().orc_ffn_hidden(fmt, _ptr(np.ascontiguousarray(gu_codes)),
+                           _ptr(np.ascontiguousarray(gu_scales)), k, f, _ptr(x), b,
+                           _ptr(xbuf), _ptr(hbuf), _ptr(z))
+    return z
+
+
+def ffn(fmt, gu_codes, gu_scales, dn_codes, dn_scales, k, f, x_fp16, row0=0, nrows=None,
+        z=None) -> np.ndarray:
+    """y[b][rows] of the decode FFN in double; W_dn is [k][f] (rows = outputs).
+    A precomputed z from ffn_hidden may be passed to sample several row sets."""
+    if z is None:
+        z = ffn_hidden(fmt, gu_codes, gu_scales, k, f, x_fp16)
+    return gemv(fmt, dn_codes, dn_scales, k, f, z, row0=row0, nrows=nrows)

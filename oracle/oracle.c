@@ -86,6 +86,34 @@ uint16_t orc_f64_to_bf16_rne(double v) {
   return sign | (uint16_t)(u >> 16);
 }
 
+/* double -> binary16, round to nearest, ties to even, in one step.  11
+ * significant bits, normal exponents -14..15, subnormal spacing 2^-24; a
+ * result of 2^16 or more (i.e. |v| >= 65520) is infinity. */
+uint16_t orc_f64_to_fp16_rne(double v) {
+  if (isnan(v)) return 0x7E00;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isinf(a)) return sign | 0x7C00;
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);   /* a = f * 2^e with f in [0.5, 1) */
+  int E = e - 1;  /* a = 1.xxx * 2^E */
+  if (E < -14) E = -14;
+  double ulp = ldexp(1.0, E - 10);
+  double res = rint(a / ulp) * ulp; /* a / ulp is exact (power of two) */
+  if (res >= 65536.0) return sign | 0x7C00;
+  if (res < ldexp(1.0, -14)) /* subnormal: res = f * 2^-24, f < 1024 */
+    return sign | (uint16_t)ldexp(res, 24);
+  int e2;
+  double m = frexp(res, &e2); /* res = m * 2^e2, m in [0.5, 1) */
+  uint16_t biased = (uint16_t)(e2 - 1 + 15);
+  uint16_t frac = (uint16_t)ldexp(2.0 * m - 1.0, 10); /* exact, < 1024 */
+  return sign | (uint16_t)(biased << 10) | frac;
+}
+
+/* SiLU(v) = v * sigmoid(v) = v / (1 + e^-v), in double. */
+double orc_silu(double v) { return v / (1.0 + exp(-v)); }
+
 /* ---------------------------------------------------------------------- */
 /* Layout, re-derived from the text of include/lowbit.h (version 1).       */
 
@@ -265,4 +293,21 @@ void orc_gemm_rows(int fmt, const uint8_t* codes, const uint16_t* scales,
     orc_gemv_rows_f64x(fmt, codes, scales, n, k, xbuf, 1, row0, nrows,
                        y + i * nrows);
   }
+}
+
+/* Decode FFN, hidden part.  h = W_gu x with W_gu [2f][k]: rows 0..f-1 are
+ * the gate projection, rows f..2f-1 the up projection; then
+ *   z[i][j] = RNE_fp16( SiLU(h[i][j]) * h[i][f + j] ),  0 <= j < f,
+ * the activation that the down projection (W_dn [k][f]) reads.  x is FP16
+ * [b][k]; xbuf holds b*k doubles, hbuf b*2f doubles; z is FP16 [b][f]. */
+void orc_ffn_hidden(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scales,
+                    int64_t k, int64_t f, const uint16_t* x_fp16, int64_t b,
+                    double* xbuf, double* hbuf, uint16_t* z_fp16) {
+  orc_gemv_rows(fmt, gu_codes, gu_scales, 2 * f, k, x_fp16, b, 0, 2 * f, xbuf, hbuf);
+  for (int64_t i = 0; i < b; ++i)
+    for (int64_t j = 0; j < f; ++j) {
+      double gate = hbuf[i * 2 * f + j];
+      double up = hbuf[i * 2 * f + f + j];
+      z_fp16[i * f + j] = orc_f64_to_fp16_rne(orc_silu(gate) * up);
+    }
 }

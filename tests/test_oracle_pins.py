@@ -374,3 +374,107 @@ def test_gemm_matches_numpy_and_gemv(fmt):
         assert np.array_equal(y[i], oracle.gemv_f64x(fmt, codes, scales, n, k, X[i])[0])
     ys = oracle.gemm(fmt, codes, scales, n, k, x, m0=2, mrows=2, row0=5, nrows=9)
     assert np.array_equal(ys, y[2:4, 5:14])
+
+
+# --------------------------------------------------------------------------
+# decode FFN: y = W_dn RNE_fp16(SiLU(W_gate x) * (W_up x))
+
+def test_f64_to_fp16_rne_matches_numpy():
+    # every finite FP16 value round-trips, and every midpoint between two
+    # neighbours rounds as numpy's direct double -> half conversion does
+    # (nearest, ties to even); random doubles over the whole range too
+    h = np.arange(0x7C00, dtype=np.uint32).astype(np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.f64_to_fp16_rne_array(v), h)
+    assert np.array_equal(oracle.f64_to_fp16_rne_array(-v), h | 0x8000)
+    mid = (v[:-1] + v[1:]) / 2  # exact in double
+    want = mid.astype(np.float16).view(np.uint16)
+    got = oracle.f64_to_fp16_rne_array(mid)
+    assert np.array_equal(got, want)
+    assert np.array_equal(got & 1, np.zeros_like(got))  # ties went to even
+    g = np.random.default_rng(21)
+    r = g.standard_normal(20000) * np.exp2(g.integers(-30, 18, 20000))
+    with np.errstate(over="ignore"):
+        want = r.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f64_to_fp16_rne_array(r), want)
+    assert oracle.f64_to_fp16_rne(65519.99) == 0x7BFF and oracle.f64_to_fp16_rne(65520.0) == 0x7C00
+
+
+def test_silu_against_expit_and_identities():
+    from scipy.special import expit
+    g = np.random.default_rng(22)
+    vs = np.concatenate([g.standard_normal(500) * 8, [0.0, 1e-300, -745.0, 745.0, 30.0, -30.0]])
+    for v in vs:
+        s = oracle.silu(v)
+        assert s == pytest.approx(v * expit(v), rel=1e-14, abs=1e-300)
+        # v * sigmoid(v) - (-v) * sigmoid(-v) = v
+        assert s - oracle.silu(-v) == pytest.approx(v, rel=1e-13, abs=1e-300)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(-1000.0) == 0.0  # e^1000 overflows to inf: v / inf
+
+
+def _ffn_weights(fmt, g, k, f):
+    """Stacked gate+up [2f][k] and down [k][f] weights with dense copies."""
+    if fmt == oracle.Q1:
+        wgu = synth.fp16_normal(g, (2 * f, k), 0.1)
+        wdn = synth.fp16_normal(g, (k, f), 0.1)
+        gu = oracle.q1_quantize(wgu)
+        dn = oracle.q1_quantize(wdn)
+        return gu, dn, _dense_q1(wgu), _dense_q1(wdn)
+    tgu, tdn = synth.ternary(g, (2 * f, k)), synth.ternary(g, (k, f))
+    sgu = synth.fp16_uniform(g, (2 * f, k // 128), 0.01, 0.2)
+    sdn = synth.fp16_uniform(g, (k, f // 128), 0.01, 0.2)
+    return (oracle.t2_pack(tgu, sgu), oracle.t2_pack(tdn, sdn),
+            _dense_t2(tgu, sgu), _dense_t2(tdn, sdn))
+
+
+@pytest.mark.parametrize("fmt", [oracle.Q1, oracle.T2])
+def test_ffn_matches_numpy_dense(fmt):
+    from scipy.special import expit
+    g = synth.rng(23)
+    k, f, b = 256, 384, 3
+    (gc, gs), (dc, ds), Wgu, Wdn = _ffn_weights(fmt, g, k, f)
+    x = synth.fp16_normal(g, (b, k))
+    X = x.view(np.float16).astype(np.float64)
+    h = X @ Wgu.T
+    zz = h[:, :f] * expit(h[:, :f]) * h[:, f:]
+    z16 = zz.astype(np.float16)
+    z = oracle.ffn_hidden(fmt, gc, gs, k, f, x)
+    assert np.array_equal(z, z16.view(np.uint16))
+    y = oracle.ffn(fmt, gc, gs, dc, ds, k, f, x)
+    ref = z16.astype(np.float64) @ Wdn.T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    ys = oracle.ffn(fmt, gc, gs, dc, ds, k, f, x, row0=100, nrows=30, z=z)
+    assert np.array_equal(ys, y[:, 100:130])
+
+
+def test_ffn_closed_forms():
+    g = synth.rng(24)
+    k, f = 128, 256
+    tgu, tdn = synth.ternary(g, (2 * f, k)), synth.ternary(g, (k, f))
+    sgu = synth.fp16_uniform(g, (2 * f, 1), 0.01, 0.2)
+    sdn = synth.fp16_uniform(g, (k, f // 128), 0.01, 0.2)
+    dc, ds = oracle.t2_pack(tdn, sdn)
+    x = synth.fp16_normal(g, (2, k))
+    # zero gate rows: SiLU(0) = 0, so z and y are exact zeros (z = -0.0
+    # where the up value is negative)
+    t0 = tgu.copy(); t0[:f] = 0
+    gc0, gs0 = oracle.t2_pack(t0, sgu)
+    assert not (oracle.ffn_hidden(oracle.T2, gc0, gs0, k, f, x) & 0x7FFF).any()
+    assert not oracle.ffn(oracle.T2, gc0, gs0, dc, ds, k, f, x).any()
+    # x = e_j: h is column j of the dequantised stacked matrix, exactly, so
+    # z[f'] = RNE_fp16(SiLU(w_gate) * w_up) from math.exp and numpy's rounding
+    gc, gs = oracle.t2_pack(tgu, sgu)
+    sv = sgu.view(np.float16).astype(np.float64)[:, 0]
+    for j in (0, 5, 127):
+        e = np.zeros((1, k), np.uint16); e[0, j] = 0x3C00
+        wg = tgu[:f, j] * sv[:f]
+        wu = tgu[f:, j] * sv[f:]
+        want = np.array([a / (1.0 + math.exp(-a)) * c for a, c in zip(wg, wu)]).astype(np.float16)
+        assert np.array_equal(oracle.ffn_hidden(oracle.T2, gc, gs, k, f, e)[0], want.view(np.uint16))
+    # gate and up are not interchangeable: the stacked order matters
+    sw = np.concatenate([tgu[f:], tgu[:f]])
+    gsw = np.concatenate([sgu[f:], sgu[:f]])
+    gc2, gs2 = oracle.t2_pack(sw, gsw)
+    assert not np.array_equal(oracle.ffn_hidden(oracle.T2, gc2, gs2, k, f, x),
+                              oracle.ffn_hidden(oracle.T2, gc, gs, k, f, x))
