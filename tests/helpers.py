@@ -54,3 +54,31 @@ def assert_close(y, ref, what=""):
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     assert e <= TOL, f"{what}: floored relative error {e:.3e} > {TOL}"
     return e
+
+
+def full_weights(fmt, n, k, seed):
+    """Seeded full-size weights for a GPU parity test: the values are drawn
+    on the device (torch's seeded generator, as bench.py does), copied to
+    the host and packed there by the oracle; the GPU gets the uploaded
+    oracle codes, so both sides read the same codes and none of the
+    oracle's inputs comes from the library.  Returns (device codes, device
+    scales, host codes, host scales)."""
+    import torch
+
+    import oracle
+    from bit_matmul_lowbit_amd import synth
+
+    if fmt == "q1":
+        w = synth.dev_fp16_normal((n, k), 0.1, seed)
+        hw = host_u16(w)
+        del w
+        hc, hs = oracle.q1_quantize(hw)
+        del hw
+    else:
+        t = synth.dev_ternary((n, k), seed)
+        s = synth.dev_fp16_uniform((n, k // 128), 0.01, 0.2, seed + 1)
+        ht, hsc = t.cpu().numpy(), host_u16(s)
+        del t, s
+        hc, hs = oracle.t2_pack(ht, hsc)
+        del ht
+    return torch.from_numpy(hc).cuda(), dev_u16(hs), hc, hs

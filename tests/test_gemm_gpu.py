@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from bit_matmul_lowbit_amd import lowbit, synth
-from tests.helpers import TOL, assert_close, dev_u16, host_u16, host_u8, say
+from tests.helpers import TOL, assert_close, dev_u16, full_weights, host_u16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -112,18 +112,12 @@ def test_full_pp512(fmt, m, n, k):
 
     say(f"gemm full {fmt} m={m} n={n} k={k}")
     seed = 1004 + n
-    if fmt == "q1":
-        w = synth.dev_fp16_normal((n, k), 0.1, seed)
-        codes, scales = lowbit.lowbit_quantize_q1(w)
-    else:
-        t = synth.dev_ternary((n, k), seed)
-        s = synth.dev_fp16_uniform((n, k // 128), 0.01, 0.2, seed + 1)
-        codes, scales = lowbit.lowbit_pack_t2(t, s)
+    codes, scales, hc, hs = full_weights(fmt, n, k, seed)
     x = synth.dev_bf16_normal((m, k), 1.0, seed + 2)
     yf = lowbit.lowbit_gemm_f32(fmt, codes, scales, n, k, x)
     yb = lowbit.lowbit_gemm(fmt, codes, scales, n, k, x)
     torch.cuda.synchronize()
-    hc, hs, hx = host_u8(codes), host_u16(scales), host_u16(x)
+    hx = host_u16(x)
     yf, yb = yf.cpu().numpy(), host_u16(yb)
     assert np.array_equal(yb, _rne_f32_to_bf16(yf))
     f = oracle.Q1 if fmt == "q1" else oracle.T2

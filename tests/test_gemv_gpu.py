@@ -124,23 +124,15 @@ FULL = [
 def test_full_size(fmt, n, k, b):
     import torch
 
-    from tests.helpers import host_u16, host_u8
+    from tests.helpers import full_weights, host_u16
 
     say(f"gemv full {fmt} n={n} k={k} b={b}")
     seed = 1000 + n + k + b
-    if fmt == "q1":
-        w = synth.dev_fp16_normal((n, k), 0.1, seed)
-        codes, scales = lowbit.lowbit_quantize_q1(w)
-        del w
-    else:
-        t = synth.dev_ternary((n, k), seed)
-        s = synth.dev_fp16_uniform((n, k // 128), 0.01, 0.2, seed + 1)
-        codes, scales = lowbit.lowbit_pack_t2(t, s)
-        del t, s
+    codes, scales, hc, hs = full_weights(fmt, n, k, seed)
     x = synth.dev_fp16_normal((b, k), 1.0, seed + 2)
     y = lowbit.lowbit_gemv(fmt, codes, scales, n, k, x)
     torch.cuda.synchronize()
-    hc, hs, hx = host_u8(codes), host_u16(scales), host_u16(x)
+    hx = host_u16(x)
     f = oracle.Q1 if fmt == "q1" else oracle.T2
     yh = y.cpu().numpy()
     if b == 1:
