@@ -41,6 +41,13 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st);
 
+// decode FFN: SiLU(gate) * up -> FP16, and the whole gated-MLP chain
+hipError_t launch_silu_mul(const float* h, int64_t f, int64_t b, uint16_t* z, hipStream_t st);
+size_t ffn_workspace_bytes(int64_t k, int64_t f, int64_t b);
+hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scales,
+                      const uint8_t* dn_codes, const uint16_t* dn_scales, int64_t k, int64_t f,
+                      const uint16_t* x, int64_t b, float* y, void* ws, hipStream_t st);
+
 hipError_t launch_gemm(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                        int64_t k, const uint16_t* x, int64_t m, void* y, bool out_f32,
                        hipStream_t st);

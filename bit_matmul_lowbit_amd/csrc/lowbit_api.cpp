@@ -162,4 +162,39 @@ int lowbit_gemm_f32(int fmt, const void* codes, const uint16_t* scales, int64_t 
   return gemm_common(fmt, codes, scales, n, k, x_bf16, m, y_f32, true, stream);
 }
 
+int lowbit_silu_mul(const float* h_f32, int64_t f, int64_t b, uint16_t* z_fp16,
+                    hipStream_t stream) {
+  if (!h_f32 || !z_fp16) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > (int64_t(1) << 20)) return LOWBIT_ERR_ARG;
+  if (f < 8 || f % 8 != 0 || f > kMaxElems / (2 * b)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(h_f32) || !aligned16(z_fp16)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_silu_mul(h_f32, f, b, z_fp16, stream));
+}
+
+size_t lowbit_ffn_workspace_bytes(int fmt, int64_t k, int64_t f, int64_t b) {
+  if (!fmt_ok(fmt) || f < 1 || f > kMaxElems || !shape_ok(2 * f, k) || !shape_ok(k, f) ||
+      b < 1 || b > 8)
+    return 0;
+  return lowbit::ffn_workspace_bytes(k, f, b);
+}
+
+int lowbit_ffn(int fmt, const void* gu_codes, const uint16_t* gu_scales, const void* dn_codes,
+               const uint16_t* dn_scales, int64_t k, int64_t f, const uint16_t* x_fp16,
+               int64_t b, float* y_f32, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  if (!fmt_ok(fmt) || !gu_codes || !gu_scales || !dn_codes || !dn_scales || !x_fp16 || !y_f32)
+    return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 8) return LOWBIT_ERR_ARG;
+  if (f < 1 || f > kMaxElems || !shape_ok(2 * f, k) || !shape_ok(k, f)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(gu_codes) || !aligned16(gu_scales) || !aligned16(dn_codes) ||
+      !aligned16(dn_scales) || !aligned16(x_fp16) || !aligned16(y_f32))
+    return LOWBIT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lowbit::ffn_workspace_bytes(k, f, b))
+    return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_ffn(fmt, static_cast<const uint8_t*>(gu_codes), gu_scales,
+                                       static_cast<const uint8_t*>(dn_codes), dn_scales, k, f,
+                                       x_fp16, b, y_f32, workspace, stream));
+}
+
 }  // extern "C"

@@ -24,7 +24,8 @@ SYMBOLS = [
     "lowbit_version", "lowbit_status_str", "lowbit_codes_bytes", "lowbit_scales_bytes",
     "lowbit_quantize_q1", "lowbit_pack_t2", "lowbit_pack", "lowbit_unpack",
     "lowbit_gemv_workspace_bytes", "lowbit_gemv_prepare", "lowbit_gemv_accumulate",
-    "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32",
+    "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32", "lowbit_silu_mul",
+    "lowbit_ffn_workspace_bytes", "lowbit_ffn",
 ]
 
 
@@ -63,6 +64,9 @@ def load() -> ctypes.CDLL:
         "lowbit_gemv": ([i, p, p, i64, i64, p, i64, p, p, sz, p], i),
         "lowbit_gemm": ([i, p, p, i64, i64, p, i64, p, p], i),
         "lowbit_gemm_f32": ([i, p, p, i64, i64, p, i64, p, p], i),
+        "lowbit_silu_mul": ([p, i64, i64, p, p], i),
+        "lowbit_ffn_workspace_bytes": ([i, i64, i64, i64], sz),
+        "lowbit_ffn": ([i, p, p, p, p, i64, i64, p, i64, p, p, sz, p], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -210,7 +214,7 @@ def lowbit_gemv(fmt, codes, scales, n: int, k: int, x, out=None, workspace=None,
 
 
 def lowbit_gemv_prepare(n: int, k: int, x, out, workspace, stream=None):
-    """Tables for x FP16 [b][k] into `workspace`; out FP32 [b][n] := 0."""
+    """x FP16 [b][k] prepared into `workspace`; out FP32 [b][n] := 0."""
     import torch
 
     x2 = x if x.dim() == 2 else x.view(1, -1)
@@ -262,4 +266,51 @@ def lowbit_gemm_f32(fmt, codes, scales, n: int, k: int, x, out=None, stream=None
                                   _dev(x, (torch.bfloat16,), "x"), m,
                                   _dev(out, (torch.float32,), "out"), _stream(stream)),
            "lowbit_gemm_f32")
+    return out
+
+
+def lowbit_silu_mul(h, out=None, stream=None):
+    """h FP32 [b][2f] (gate | up) -> z FP16 [b][f] = SiLU(gate) * up."""
+    import torch
+
+    h2 = h if h.dim() == 2 else h.view(1, -1)
+    b, f2 = h2.shape
+    if f2 % 2:
+        raise ValueError("h must have 2f columns")
+    f = f2 // 2
+    if out is None:
+        out = torch.empty((b, f), dtype=torch.float16, device=h.device)
+    _check(load().lowbit_silu_mul(_dev(h2, (torch.float32,), "h"), f, b,
+                                  _dev(out, (torch.float16,), "out"), _stream(stream)),
+           "lowbit_silu_mul")
+    return out
+
+
+def lowbit_ffn_workspace_bytes(fmt, k: int, f: int, b: int) -> int:
+    return int(load().lowbit_ffn_workspace_bytes(_fmt(fmt), k, f, b))
+
+
+def lowbit_ffn(fmt, gu_codes, gu_scales, dn_codes, dn_scales, k: int, f: int, x, out=None,
+               workspace=None, stream=None):
+    """Decode FFN: x FP16 [b][k] -> y FP32 [b][k] = W_dn (SiLU(W_gate x) * (W_up x)),
+    W_gu = [gate; up] stacked as [2f][k], W_dn [k][f]."""
+    import torch
+
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    b = x2.shape[0]
+    if x2.shape[1] != k:
+        raise ValueError("x must have k columns")
+    if out is None:
+        out = torch.empty((b, k), dtype=torch.float32, device=x.device)
+    need = lowbit_ffn_workspace_bytes(fmt, k, f, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(load().lowbit_ffn(_fmt(fmt), _dev(gu_codes, (torch.uint8,), "gu_codes"),
+                             _dev(gu_scales, (torch.float16, torch.int16), "gu_scales"),
+                             _dev(dn_codes, (torch.uint8,), "dn_codes"),
+                             _dev(dn_scales, (torch.float16, torch.int16), "dn_scales"),
+                             k, f, _dev(x2, (torch.float16,), "x"), b,
+                             _dev(out, (torch.float32,), "out"),
+                             _dev(workspace, (torch.uint8,), "workspace"),
+                             workspace.numel(), _stream(stream)), "lowbit_ffn")
     return out

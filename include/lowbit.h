@@ -212,6 +212,43 @@ int lowbit_gemm_f32(int fmt, const void* codes, const uint16_t* scales,
                     int64_t n, int64_t k, const uint16_t* x_bf16, int64_t m,
                     float* y_f32, hipStream_t stream);
 
+/* SiLU-gated product of a decode FFN  [P2 "Como funciona la compresion":
+ * the MLP projections are low-bit; P5 "Detalles tecnicos": decode kernels
+ * were tuned at the FFN level.  The gated MLP form is that of the Qwen
+ * family the models derive from; the pages do not spell it out.]
+ *   z[i][j] = RNE_fp16( SiLU(h[i][j]) * h[i][f + j] ),  0 <= j < f, 0 <= i < b
+ *   h_f32  : [b][2f] row-major FP32 (device, read-only): columns 0..f-1 the
+ *            gate projection, f..2f-1 the up projection
+ *   z_fp16 : [b][f] row-major FP16 (device, written)
+ * SiLU(v) = v / (1 + e^-v) is evaluated in FP32 with the device expf; the
+ * product is rounded once to FP16 (nearest-even; beyond the FP16 range it
+ * becomes +-inf; a value that rounds to zero may come out as +0 or -0).
+ * f must be a multiple of 8. */
+int lowbit_silu_mul(const float* h_f32, int64_t f, int64_t b, uint16_t* z_fp16,
+                    hipStream_t stream);
+
+/* Workspace bytes lowbit_ffn needs for (fmt, k, f, b); 0 on a bad shape. */
+size_t lowbit_ffn_workspace_bytes(int fmt, int64_t k, int64_t f, int64_t b);
+
+/* Decode FFN (gated MLP) on one activation batch, as one stream-ordered
+ * chain (no host synchronisation; it may be captured in a HIP graph):
+ *   h = W_gu x               W_gu: [2f][k] codes + scales (gate rows 0..f-1,
+ *                                  up rows f..2f-1), the lowbit_gemv kernels
+ *   z = lowbit_silu_mul(h)   FP16 [b][f]
+ *   y = W_dn z               W_dn: [k][f] codes + scales (k outputs)
+ *   x_fp16    : [b][k] FP16 (device, read-only), 1 <= b <= 8
+ *   y_f32     : [b][k] FP32 (device, written)
+ *   workspace : at least lowbit_ffn_workspace_bytes(fmt, k, f, b) bytes of
+ *               device scratch, contents ignored on entry and clobbered.
+ * Both matrices use format fmt; k and f must be multiples of 128.  As in
+ * lowbit_gemv, K-slices are combined with atomic adds, so the last bits of
+ * h and y may differ from run to run, and so may a z value that lies on an
+ * FP16 rounding boundary. */
+int lowbit_ffn(int fmt, const void* gu_codes, const uint16_t* gu_scales,
+               const void* dn_codes, const uint16_t* dn_scales, int64_t k, int64_t f,
+               const uint16_t* x_fp16, int64_t b, float* y_f32, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

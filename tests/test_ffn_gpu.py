@@ -1,0 +1,145 @@
+"""GPU parity of the decode FFN (gated MLP) against the double-precision oracle.
+
+y = W_dn RNE_fp16(SiLU(W_gate x) * (W_up x)), gate and up stacked in one
+[2f][k] matrix [P2 "Como funciona la compresion": the MLP projections are
+low-bit; P5 "Detalles tecnicos": FFN-level decode kernels].
+
+Tolerances, from the arithmetic:
+* lowbit_silu_mul, given h exactly, computes SiLU and the product in FP32
+  (a few FP32 ulps, well under 1e-6 relative) and rounds once to FP16: its
+  output must be the FP16 rounding of the exact double value, except where
+  that value lies within 1e-6 (relative) of an FP16 rounding boundary,
+  where either neighbour is accepted; a value that rounds to zero may be
+  either zero;
+* the whole chain adds the FP32 GEMV error to h, so a z value whose exact
+  double lies near an FP16 rounding boundary can round one FP16 ulp the
+  other way.  Each such flip moves an output by |w| * ulp(z) and the flips
+  are few and of random sign: their sum stays below 2e-4 * rms(y) at every
+  shape here (at f = 17408 a CPU model of the FP32 chain puts it at
+  ~2e-5 * rms(y)).  So every output must satisfy
+    |y - y_oracle| <= 1e-3 * max(|y_oracle|, 0.01 rms(y_oracle)) + 2e-4 rms(y_oracle),
+  the GEMV's floored bound plus that FP16-intermediate term.  A wrong gate,
+  order, scale or layout errs by O(rms(y)).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_matmul_lowbit_amd import lowbit, synth
+from tests.helpers import TOL, dev_u16, full_weights, host_u16, say
+
+pytestmark = pytest.mark.gpu
+
+FFN_TERM = 2e-4  # FP16-intermediate allowance, relative to rms(y) per output vector
+
+
+def _ffn_ok(y, ref, what):
+    y = np.atleast_2d(np.asarray(y, np.float64))
+    ref = np.atleast_2d(ref)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    for i, (yr, rr) in enumerate(zip(y, ref)):
+        rms = np.sqrt(np.mean(rr * rr))
+        bound = TOL * np.maximum(np.abs(rr), 0.01 * rms) + FFN_TERM * rms
+        worst = np.max(np.abs(yr - rr) - bound)
+        assert worst <= 0, f"{what} batch row {i}: exceeds the bound by {worst:.3e} (rms {rms:.3e})"
+
+
+def _fp16_bracket(z64, rho=1e-6):
+    """FP16 roundings of z64 * (1 -+ rho): equal unless z64 is within rho of a
+    rounding boundary."""
+    a = oracle.f64_to_fp16_rne_array(z64 * (1 - rho))
+    b = oracle.f64_to_fp16_rne_array(z64 * (1 + rho))
+    return a, b
+
+
+def test_silu_mul_matches_oracle():
+    import torch
+
+    say("silu_mul b=3 f=1024 plus edge values")
+    g = np.random.default_rng(71)
+    b, f = 3, 1024
+    h = (g.standard_normal((b, 2 * f)) * 6).astype(np.float32)
+    # edges: zeros of both signs, exp overflow (v < -88), large products
+    # (beyond the FP16 range), tiny products (FP16 subnormals)
+    h[0, :8] = [0.0, -0.0, -100.0, -88.5, 88.0, 300.0, 1e-4, -1e-4]
+    h[0, f:f + 8] = [1.5, -2.0, 3.0, -1.0, 2.0, 400.0, 1e-3, 2e-3]
+    z = host_u16(lowbit.lowbit_silu_mul(torch.from_numpy(h).cuda()))
+    torch.cuda.synchronize()
+    h64 = h.astype(np.float64)
+    z64 = np.array([[oracle.silu(v) for v in row] for row in h64[:, :f]]) * h64[:, f:]
+    lo, hi = _fp16_bracket(z64)
+    # a value that rounds to zero may come out as either zero: SiLU(v)
+    # underflows in FP32 for v < -88, and the sign of a zero activation is
+    # not part of the contract (it only multiplies weights)
+    zero = ((lo & 0x7FFF) == 0) & ((z & 0x7FFF) == 0)
+    ok = (z == lo) | (z == hi) | zero
+    bad = np.argwhere(~ok)[:4].tolist()
+    assert ok.all(), (f"{(~ok).sum()} values off, first at {bad}: got "
+                      f"{[hex(z[i, j]) for i, j in bad]}, want {[hex(lo[i, j]) for i, j in bad]}")
+    assert (lo != hi).sum() < 0.01 * z.size  # the allowance is rarely used
+    assert z[0, 5] == 0x7C00  # SiLU(300) * 400 is beyond FP16: +inf
+
+
+SMALL = [(128, 128, 1), (256, 384, 2), (384, 256, 3), (512, 640, 5), (1024, 512, 8),
+         (256, 1024, 1), (640, 256, 4)]
+
+
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("k,f,b", SMALL)
+def test_ffn_small_shapes(fmt, k, f, b):
+    import torch
+
+    say(f"ffn {fmt} k={k} f={f} b={b}")
+    g = synth.rng(2000 + k + f + b)
+    if fmt == "q1":
+        gu = oracle.q1_quantize(synth.fp16_normal(g, (2 * f, k), 0.1))
+        dn = oracle.q1_quantize(synth.fp16_normal(g, (k, f), 0.1))
+    else:
+        gu = oracle.t2_pack(synth.ternary(g, (2 * f, k)), synth.fp16_uniform(g, (2 * f, k // 128), 0.01, 0.2))
+        dn = oracle.t2_pack(synth.ternary(g, (k, f)), synth.fp16_uniform(g, (k, f // 128), 0.01, 0.2))
+    x = synth.fp16_normal(g, (b, k))
+    of = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.ffn(of, gu[0], gu[1], dn[0], dn[1], k, f, x)
+    y = lowbit.lowbit_ffn(fmt, torch.from_numpy(gu[0]).cuda(), dev_u16(gu[1]),
+                          torch.from_numpy(dn[0]).cuda(), dev_u16(dn[1]), k, f, dev_u16(x))
+    torch.cuda.synchronize()
+    _ffn_ok(y.cpu().numpy(), ref, f"ffn {fmt} k={k} f={f} b={b}")
+
+
+def test_ffn_zero_gate_gives_exact_zeros():
+    import torch
+
+    say("ffn zero gate")
+    g = synth.rng(2100)
+    k, f, b = 256, 256, 3
+    t = synth.ternary(g, (2 * f, k))
+    t[:f] = 0
+    gu = oracle.t2_pack(t, synth.fp16_uniform(g, (2 * f, k // 128), 0.01, 0.2))
+    dn = oracle.t2_pack(synth.ternary(g, (k, f)), synth.fp16_uniform(g, (k, f // 128), 0.01, 0.2))
+    x = synth.fp16_normal(g, (b, k))
+    y = lowbit.lowbit_ffn("t2", torch.from_numpy(gu[0]).cuda(), dev_u16(gu[1]),
+                          torch.from_numpy(dn[0]).cuda(), dev_u16(dn[1]), k, f, dev_u16(x))
+    torch.cuda.synchronize()
+    assert not y.cpu().numpy().any()
+
+
+FULL = [("q1", 5120, 17408, 1), ("q1", 5120, 17408, 5), ("t2", 2048, 6144, 1)]
+
+
+@pytest.mark.parametrize("fmt,k,f,b", FULL)
+def test_ffn_full_shapes(fmt, k, f, b):
+    import torch
+
+    say(f"ffn full {fmt} k={k} f={f} b={b}")
+    seed = 3000 + k + f + b
+    guc, gus, hguc, hgus = full_weights(fmt, 2 * f, k, seed)
+    dnc, dns, hdnc, hdns = full_weights(fmt, k, f, seed + 7)
+    x = synth.dev_fp16_normal((b, k), 1.0, seed + 3)
+    y = lowbit.lowbit_ffn(fmt, guc, gus, dnc, dns, k, f, x)
+    torch.cuda.synchronize()
+    of = oracle.Q1 if fmt == "q1" else oracle.T2
+    hx = host_u16(x)
+    # every output (the bound needs rms(y) of the whole vector); the oracle
+    # takes a few seconds at these sizes
+    ref = oracle.ffn(of, hguc, hgus, hdnc, hdns, k, f, hx)
+    _ffn_ok(y.cpu().numpy(), ref, f"ffn full {fmt} k={k} f={f} b={b}")

@@ -130,3 +130,32 @@ def test_validation_returns_before_launch(lib):
     assert lib.lowbit_gemm_f32(T2, good, null, 16, 128, good, 4, good, st) == ARG
     # a huge shape is refused, not overflowed
     assert lib.lowbit_gemv(Q1, good, good, 1 << 40, 128, good, 1, good, good, 1 << 20, st) == SHAPE
+
+
+def test_ffn_workspace_query_and_validation(lib):
+    def a256(v):
+        return (v + 255) // 256 * 256
+    # [x prepared for W_gu][h FP32 b x 2f][z prepared for W_dn], 256-aligned parts
+    for b in (1, 2, 5, 8):
+        for k, f in ((5120, 17408), (2048, 6144), (128, 128)):
+            want = (a256(lowbit.lowbit_gemv_workspace_bytes("q1", 2 * f, k, b)) + a256(b * 2 * f * 4)
+                    + a256(lowbit.lowbit_gemv_workspace_bytes("q1", k, f, b)))
+            assert lowbit.lowbit_ffn_workspace_bytes("q1", k, f, b) == want
+    assert lowbit.lowbit_ffn_workspace_bytes("q1", 5120, 100, 1) == 0   # f % 128
+    assert lowbit.lowbit_ffn_workspace_bytes("q1", 5000, 128, 1) == 0   # k % 128
+    assert lowbit.lowbit_ffn_workspace_bytes("q1", 128, 128, 9) == 0
+    assert lowbit.lowbit_ffn_workspace_bytes("q1", 128, 1 << 62, 1) == 0
+    good, bad_align, null, st = P(0x10000), P(0x10008), P(0), P(0)
+    big = 1 << 30
+    assert lib.lowbit_ffn(Q1, good, good, good, good, 128, 128, good, 0, good, good, big, st) == ARG
+    assert lib.lowbit_ffn(Q1, good, good, null, good, 128, 128, good, 1, good, good, big, st) == ARG
+    assert lib.lowbit_ffn(Q1, good, good, good, good, 128, 200, good, 1, good, good, big, st) == SHAPE
+    assert lib.lowbit_ffn(Q1, good, good, good, good, 130, 128, good, 1, good, good, big, st) == SHAPE
+    assert lib.lowbit_ffn(Q1, good, good, good, good, 128, 128, bad_align, 1, good, good, big, st) == ALIGN
+    assert lib.lowbit_ffn(Q1, good, good, good, good, 128, 128, good, 1, good, good, 64, st) == WS
+    assert lib.lowbit_ffn(Q1, good, good, good, good, 128, 128, good, 1, good, null, big, st) == WS
+    # silu_mul
+    assert lib.lowbit_silu_mul(null, 128, 1, good, st) == ARG
+    assert lib.lowbit_silu_mul(good, 128, 0, good, st) == ARG
+    assert lib.lowbit_silu_mul(good, 12, 1, good, st) == SHAPE
+    assert lib.lowbit_silu_mul(good, 128, 1, bad_align, st) == ALIGN
