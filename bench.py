@@ -18,7 +18,9 @@ Printed: one JSON line with
              rocprofv3 counters gave for the same kernel source, or null
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
   secondary  the other workloads: decode GEMVs (fused FFN shapes, batch
-             sweep), the FP16 -> Q1 quantiser and the pp512 prefill GEMMs;
+             sweep), the decode FFN chain (gate+up GEMV, SiLU-gated
+             product, down GEMV; eager and as a graph), the FP16 -> Q1
+             quantiser and the pp512 prefill GEMMs;
              for the GEMVs also the per-step time of a HIP graph that holds
              one step per rotated copy (small matrices are otherwise timed
              by the host's launch rate); the GEMMs' `us` is the device time
@@ -171,6 +173,60 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
     del copies
     torch.cuda.empty_cache()
     return out
+
+
+def time_ffn(fmt, k, f, b, seed, steps, warmup):
+    """Decode FFN (lowbit_ffn: gate+up GEMV, SiLU-gated product, down GEMV)
+    over rotated copies of both matrices: per-step time of eager calls and
+    of a HIP graph holding one step per copy."""
+    import torch
+
+    from bit_matmul_lowbit_amd import lowbit, synth
+
+    gu_c, gu_s = make_weights(fmt, 2 * f, k, seed)
+    dn_c, dn_s = make_weights(fmt, k, f, seed + 7)
+    wbytes = gu_c.numel() + gu_s.numel() * 2 + dn_c.numel() + dn_s.numel() * 2
+    r = max(1, math.ceil(ROTATE_BYTES / wbytes))
+    copies = [(gu_c.clone(), gu_s.clone(), dn_c.clone(), dn_s.clone()) for _ in range(r)]
+    del gu_c, gu_s, dn_c, dn_s
+    x = synth.dev_fp16_normal((b, k), 1.0, seed + 3)
+    y = torch.empty((b, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lowbit.lowbit_ffn_workspace_bytes(fmt, k, f, b), dtype=torch.uint8, device="cuda")
+
+    def step(i, stream=None):
+        a, bs, c, d = copies[i % len(copies)]
+        lowbit.lowbit_ffn(fmt, a, bs, c, d, k, f, x, out=y, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) / steps * 1e3
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(len(copies)):
+                step(i, stream=cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) / (reps * len(copies)) * 1e3
+    del g, copies
+    torch.cuda.empty_cache()
+    return {"weight_bytes": wbytes, "eager_us": round(eager_ms * 1e3, 2),
+            "graph_us_per_step": round(graph_ms * 1e3, 2),
+            "graph_gbs": round(wbytes / (graph_ms * 1e-3) / 1e9, 1)}
 
 
 def time_quantize(n, k, seed, steps, warmup):
@@ -401,6 +457,12 @@ def main():
         sec["q1_quantize_151936x5120"] = {"gbs": round(q["gbs"], 1), "us": round(q["ms"] * 1e3, 1),
                                           "bytes_moved": q["bytes_moved"]}
         log(f"[bench] quantize: {sec['q1_quantize_151936x5120']}")
+        for key, (ff, kf, fff, bf) in {
+                "ffn_q1_27b_k5120_f17408_b1": ("q1", 5120, 17408, 1),
+                "ffn_q1_27b_k5120_f17408_b5": ("q1", 5120, 17408, 5),
+                "ffn_t2_1p7b_k2048_f6144_b1": ("t2", 2048, 6144, 1)}.items():
+            sec[key] = time_ffn(ff, kf, fff, bf, 1100 + fff + bf, 30, 5)
+            log(f"[bench] {key}: {sec[key]}")
         for key, (f2, m2, n2, k2) in {"gemm_pp512_t2_512x6144x2048": ("t2", 512, 6144, 2048),
                                        "gemm_pp512_q1_512x2048x6144": ("q1", 512, 2048, 6144)}.items():
             g = time_gemm(f2, m2, n2, k2, 1004 + n2, 50, 10)
