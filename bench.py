@@ -19,7 +19,9 @@ Printed: one JSON line with
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
   secondary  the other workloads: decode GEMVs (fused FFN shapes, batch
              sweep), the decode FFN chain (gate+up GEMV, SiLU-gated
-             product, down GEMV; eager and as a graph), the FP16 -> Q1
+             product, down GEMV; eager and as a graph), the two ends of
+             a decode step (8-row embedding gather; LM head with top-1
+             against the GEMV alone), the FP16 -> Q1
              quantiser and the pp512 prefill GEMMs;
              for the GEMVs also the per-step time of a HIP graph that holds
              one step per rotated copy (small matrices are otherwise timed
@@ -227,6 +229,63 @@ def time_ffn(fmt, k, f, b, seed, steps, warmup):
     return {"weight_bytes": wbytes, "eager_us": round(eager_ms * 1e3, 2),
             "graph_us_per_step": round(graph_ms * 1e3, 2),
             "graph_gbs": round(wbytes / (graph_ms * 1e-3) / 1e9, 1)}
+
+
+def time_ends(n, k, seed):
+    """The two ends of a decode step on the ternary LM-head-sized matrix:
+    gathering 8 embedding rows, and the LM head with its top-1 (GEMV +
+    argmax) against the GEMV alone; graphs over rotated weight copies."""
+    import torch
+
+    from bit_matmul_lowbit_amd import lowbit, synth
+
+    codes, scales = make_weights("t2", n, k, seed)
+    copies, wbytes = rotated_copies(codes, scales)
+    del codes, scales
+    x = synth.dev_fp16_normal((1, k), 1.0, seed + 2)
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    idx = torch.empty(1, dtype=torch.int32, device="cuda")
+    val = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lowbit.lowbit_lm_head_workspace_bytes("t2", n, k, 1), dtype=torch.uint8, device="cuda")
+    ids = torch.tensor([11, 4093, 77777, 151000, 5, 99999, 123456, 2048], dtype=torch.int32, device="cuda")
+    emb = torch.empty((ids.numel(), k), dtype=torch.float16, device="cuda")
+
+    def graph_us(body):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(len(copies)):
+                    body(i, cap)
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / (3 * len(copies)) * 1e6
+        del g
+        return round(us, 2)
+
+    def lm_head(i, st):
+        c, s = copies[i]
+        lowbit.lowbit_lm_head("t2", c, s, n, k, x, out=y, idx=idx, val=val, workspace=ws, stream=st)
+
+    def gemv_only(i, st):
+        c, s = copies[i]
+        lowbit.lowbit_gemv("t2", c, s, n, k, x, out=y, workspace=ws, stream=st)
+
+    def embed(i, st):
+        c, s = copies[i]
+        lowbit.lowbit_embed("t2", c, s, n, k, ids, out=emb, stream=st)
+
+    out = {"lm_head_argmax_us": graph_us(lm_head), "lm_head_gemv_only_us": graph_us(gemv_only),
+           "embed_8_rows_us": graph_us(embed)}
+    del copies
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_quantize(n, k, seed, steps, warmup):
@@ -463,6 +522,8 @@ def main():
                 "ffn_t2_1p7b_k2048_f6144_b1": ("t2", 2048, 6144, 1)}.items():
             sec[key] = time_ffn(ff, kf, fff, bf, 1100 + fff + bf, 30, 5)
             log(f"[bench] {key}: {sec[key]}")
+        sec["ends_t2_151936x5120_b1"] = time_ends(151936, 5120, 1900)
+        log(f"[bench] ends_t2_151936x5120_b1: {sec['ends_t2_151936x5120_b1']}")
         for key, (f2, m2, n2, k2) in {"gemm_pp512_t2_512x6144x2048": ("t2", 512, 6144, 2048),
                                        "gemm_pp512_q1_512x2048x6144": ("q1", 512, 2048, 6144)}.items():
             g = time_gemm(f2, m2, n2, k2, 1004 + n2, 50, 10)

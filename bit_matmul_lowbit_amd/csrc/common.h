@@ -48,6 +48,18 @@ hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scale
                       const uint8_t* dn_codes, const uint16_t* dn_scales, int64_t k, int64_t f,
                       const uint16_t* x, int64_t b, float* y, void* ws, hipStream_t st);
 
+// the ends of a decode step: embedding-row gather, top-1 of the LM head
+hipError_t launch_embed(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                        int64_t k, const int32_t* ids, int64_t count, uint16_t* out,
+                        hipStream_t st);
+size_t argmax_workspace_bytes(int64_t n, int64_t b);
+hipError_t launch_argmax(const float* y, int64_t n, int64_t b, int32_t* idx, float* val,
+                         void* ws, hipStream_t st);
+size_t lm_head_workspace_bytes(int64_t n, int64_t k, int64_t b);
+hipError_t launch_lm_head(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                          int64_t k, const uint16_t* x, int64_t b, float* y, int32_t* idx,
+                          float* val, void* ws, hipStream_t st);
+
 hipError_t launch_gemm(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                        int64_t k, const uint16_t* x, int64_t m, void* y, bool out_f32,
                        hipStream_t st);

@@ -197,4 +197,58 @@ int lowbit_ffn(int fmt, const void* gu_codes, const uint16_t* gu_scales, const v
                                        x_fp16, b, y_f32, workspace, stream));
 }
 
+int lowbit_embed(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                 const int32_t* ids, int64_t count, uint16_t* out_fp16, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !ids || !out_fp16) return LOWBIT_ERR_ARG;
+  if (count < 1 || count > (int64_t(1) << 31) - 1) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k) || n > (int64_t(1) << 31) - 1) return LOWBIT_ERR_SHAPE;
+  if (count > kMaxElems / k) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(out_fp16) || (reinterpret_cast<uintptr_t>(scales) & 1u) ||
+      (reinterpret_cast<uintptr_t>(ids) & 3u))
+    return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_embed(fmt, static_cast<const uint8_t*>(codes), scales, n, k,
+                                         ids, count, out_fp16, stream));
+}
+
+size_t lowbit_argmax_workspace_bytes(int64_t n, int64_t b) {
+  if (n < 1 || n > (int64_t(1) << 31) - 1 || b < 1 || b > 65535) return 0;
+  return lowbit::argmax_workspace_bytes(n, b);
+}
+
+int lowbit_argmax(const float* y_f32, int64_t n, int64_t b, int32_t* idx_out, float* val_out,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!y_f32 || !idx_out) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 65535) return LOWBIT_ERR_ARG;
+  if (n < 1 || n > (int64_t(1) << 31) - 1 || n > kMaxElems / b) return LOWBIT_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(y_f32) & 3u) || (reinterpret_cast<uintptr_t>(idx_out) & 3u) ||
+      (reinterpret_cast<uintptr_t>(val_out) & 3u))
+    return LOWBIT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lowbit::argmax_workspace_bytes(n, b))
+    return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_argmax(y_f32, n, b, idx_out, val_out, workspace, stream));
+}
+
+size_t lowbit_lm_head_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b) {
+  if (!fmt_ok(fmt) || !shape_ok(n, k) || n > (int64_t(1) << 31) - 1 || b < 1 || b > 8) return 0;
+  return lowbit::lm_head_workspace_bytes(n, k, b);
+}
+
+int lowbit_lm_head(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                   const uint16_t* x_fp16, int64_t b, float* y_f32, int32_t* idx_out,
+                   float* val_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !x_fp16 || !y_f32 || !idx_out) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 8) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k) || n > (int64_t(1) << 31) - 1) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_fp16) || !aligned16(y_f32) ||
+      (reinterpret_cast<uintptr_t>(idx_out) & 3u) || (reinterpret_cast<uintptr_t>(val_out) & 3u))
+    return LOWBIT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lowbit::lm_head_workspace_bytes(n, k, b))
+    return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_lm_head(fmt, static_cast<const uint8_t*>(codes), scales, n, k,
+                                           x_fp16, b, y_f32, idx_out, val_out, workspace,
+                                           stream));
+}
+
 }  // extern "C"

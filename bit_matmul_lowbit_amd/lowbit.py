@@ -25,7 +25,8 @@ SYMBOLS = [
     "lowbit_quantize_q1", "lowbit_pack_t2", "lowbit_pack", "lowbit_unpack",
     "lowbit_gemv_workspace_bytes", "lowbit_gemv_prepare", "lowbit_gemv_accumulate",
     "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32", "lowbit_silu_mul",
-    "lowbit_ffn_workspace_bytes", "lowbit_ffn",
+    "lowbit_ffn_workspace_bytes", "lowbit_ffn", "lowbit_embed", "lowbit_argmax_workspace_bytes",
+    "lowbit_argmax", "lowbit_lm_head_workspace_bytes", "lowbit_lm_head",
 ]
 
 
@@ -67,6 +68,11 @@ def load() -> ctypes.CDLL:
         "lowbit_silu_mul": ([p, i64, i64, p, p], i),
         "lowbit_ffn_workspace_bytes": ([i, i64, i64, i64], sz),
         "lowbit_ffn": ([i, p, p, p, p, i64, i64, p, i64, p, p, sz, p], i),
+        "lowbit_embed": ([i, p, p, i64, i64, p, i64, p, p], i),
+        "lowbit_argmax_workspace_bytes": ([i64, i64], sz),
+        "lowbit_argmax": ([p, i64, i64, p, p, p, sz, p], i),
+        "lowbit_lm_head_workspace_bytes": ([i, i64, i64, i64], sz),
+        "lowbit_lm_head": ([i, p, p, i64, i64, p, i64, p, p, p, p, sz, p], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -314,3 +320,68 @@ def lowbit_ffn(fmt, gu_codes, gu_scales, dn_codes, dn_scales, k: int, f: int, x,
                              _dev(workspace, (torch.uint8,), "workspace"),
                              workspace.numel(), _stream(stream)), "lowbit_ffn")
     return out
+
+
+def lowbit_embed(fmt, codes, scales, n: int, k: int, ids, out=None, stream=None):
+    """Rows ids (int32 [count]) of W [n][k], dequantised to FP16 [count][k]."""
+    import torch
+
+    count = ids.numel()
+    if out is None:
+        out = torch.empty((count, k), dtype=torch.float16, device=ids.device)
+    _check(load().lowbit_embed(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                               _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                               _dev(ids, (torch.int32,), "ids"), count,
+                               _dev(out, (torch.float16,), "out"), _stream(stream)),
+           "lowbit_embed")
+    return out
+
+
+def lowbit_argmax(y, idx=None, val=None, workspace=None, stream=None):
+    """Top-1 of each row of y FP32 [b][n] -> (idx int32 [b], val FP32 [b])."""
+    import torch
+
+    y2 = y if y.dim() == 2 else y.view(1, -1)
+    b, n = y2.shape
+    if idx is None:
+        idx = torch.empty(b, dtype=torch.int32, device=y.device)
+    if val is None:
+        val = torch.empty(b, dtype=torch.float32, device=y.device)
+    need = int(load().lowbit_argmax_workspace_bytes(n, b))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=y.device)
+    _check(load().lowbit_argmax(_dev(y2, (torch.float32,), "y"), n, b,
+                                _dev(idx, (torch.int32,), "idx"), _dev(val, (torch.float32,), "val"),
+                                _dev(workspace, (torch.uint8,), "workspace"), workspace.numel(),
+                                _stream(stream)), "lowbit_argmax")
+    return idx, val
+
+
+def lowbit_lm_head_workspace_bytes(fmt, n: int, k: int, b: int) -> int:
+    return int(load().lowbit_lm_head_workspace_bytes(_fmt(fmt), n, k, b))
+
+
+def lowbit_lm_head(fmt, codes, scales, n: int, k: int, x, out=None, idx=None, val=None,
+                   workspace=None, stream=None):
+    """Logits y FP32 [b][n] = W.x and their top-1 (idx int32 [b], val FP32 [b])."""
+    import torch
+
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    b = x2.shape[0]
+    if out is None:
+        out = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty(b, dtype=torch.int32, device=x.device)
+    if val is None:
+        val = torch.empty(b, dtype=torch.float32, device=x.device)
+    need = lowbit_lm_head_workspace_bytes(fmt, n, k, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(load().lowbit_lm_head(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                                 _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                                 _dev(x2, (torch.float16,), "x"), b,
+                                 _dev(out, (torch.float32,), "out"),
+                                 _dev(idx, (torch.int32,), "idx"), _dev(val, (torch.float32,), "val"),
+                                 _dev(workspace, (torch.uint8,), "workspace"), workspace.numel(),
+                                 _stream(stream)), "lowbit_lm_head")
+    return out, idx, val

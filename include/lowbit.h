@@ -249,6 +249,47 @@ int lowbit_ffn(int fmt, const void* gu_codes, const uint16_t* gu_scales,
                const uint16_t* x_fp16, int64_t b, float* y_f32, void* workspace,
                size_t workspace_bytes, hipStream_t stream);
 
+/* Embedding-row gather  [P2 "Como funciona la compresion", P4: the
+ * embeddings are low-bit too]: the rows ids[0..count) of W [n][k], each
+ * dequantised exactly as lowbit_unpack does (+s, -s, or +0 for a ternary
+ * zero).
+ *   ids      : [count] int32 row indices (device, read-only); an id outside
+ *              [0, n) gives a row of zeros (ids are not checked on the host)
+ *   out_fp16 : [count][k] row-major FP16 (device, written) */
+int lowbit_embed(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                 const int32_t* ids, int64_t count, uint16_t* out_fp16, hipStream_t stream);
+
+/* Workspace bytes lowbit_argmax needs for (n, b); 0 on a bad shape. */
+size_t lowbit_argmax_workspace_bytes(int64_t n, int64_t b);
+
+/* Top-1 of each row of y  [P5 "Detalles tecnicos": decode is checked by
+ * top-1 token match].
+ *   y_f32   : [b][n] FP32 (device, read-only), n < 2^31, b <= 65535
+ *   idx_out : [b] int32 (device, written): the index of the largest value;
+ *             among equal values the lowest index; a NaN counts as larger
+ *             than every number (as numpy's and torch's argmax do); -0 and
+ *             +0 are equal
+ *   val_out : [b] FP32 (device, written) y at that index, or NULL
+ * Two launches (per-part maxima into the workspace, then one work-group
+ * per row); the workspace contents are ignored on entry. */
+int lowbit_argmax(const float* y_f32, int64_t n, int64_t b, int32_t* idx_out, float* val_out,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes lowbit_lm_head needs for (fmt, n, k, b); 0 on a bad shape. */
+size_t lowbit_lm_head_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b);
+
+/* LM head with its top-1 token: lowbit_gemv followed by lowbit_argmax on the
+ * same stream, one workspace for both.
+ *   y_f32   : [b][n] FP32 logits (device, written)
+ *   idx_out : [b] int32, val_out : [b] FP32 or NULL (device, written)
+ * Because the GEMV's K-slices are combined with atomic adds, two logits
+ * that differ by less than its rounding error may come out in either
+ * order from run to run. */
+int lowbit_lm_head(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                   const uint16_t* x_fp16, int64_t b, float* y_f32, int32_t* idx_out,
+                   float* val_out, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -159,3 +159,36 @@ def test_ffn_workspace_query_and_validation(lib):
     assert lib.lowbit_silu_mul(good, 128, 0, good, st) == ARG
     assert lib.lowbit_silu_mul(good, 12, 1, good, st) == SHAPE
     assert lib.lowbit_silu_mul(good, 128, 1, bad_align, st) == ALIGN
+
+
+def test_ends_of_step_queries_and_validation(lib):
+    # argmax parts: ceil(n / 1024) capped at 256, 8 bytes each per batch row
+    for n, b in ((151936, 1), (151936, 8), (1000, 3), (1, 1)):
+        parts = min(256, max(1, (n + 1023) // 1024))
+        assert lowbit.load().lowbit_argmax_workspace_bytes(n, b) == (b * parts * 8 + 255) // 256 * 256
+    assert lowbit.load().lowbit_argmax_workspace_bytes(0, 1) == 0
+    assert lowbit.load().lowbit_argmax_workspace_bytes(1 << 31, 1) == 0
+    g = lowbit.lowbit_gemv_workspace_bytes("t2", 151936, 5120, 1)
+    assert lowbit.lowbit_lm_head_workspace_bytes("t2", 151936, 5120, 1) == (
+        (g + 255) // 256 * 256 + lowbit.load().lowbit_argmax_workspace_bytes(151936, 1))
+    assert lowbit.lowbit_lm_head_workspace_bytes("t2", 151936, 5120, 9) == 0
+    good, bad_align, null, st = P(0x10000), P(0x10008), P(0), P(0)
+    odd = P(0x10002)
+    big = 1 << 30
+    # embed
+    assert lib.lowbit_embed(Q1, good, good, 16, 128, null, 4, good, st) == ARG
+    assert lib.lowbit_embed(Q1, good, good, 16, 128, good, 0, good, st) == ARG
+    assert lib.lowbit_embed(Q1, good, good, 16, 100, good, 4, good, st) == SHAPE
+    assert lib.lowbit_embed(Q1, good, good, 16, 128, odd, 4, good, st) == ALIGN
+    assert lib.lowbit_embed(T2, good, good, 16, 128, good, 4, bad_align, st) == ALIGN
+    # argmax
+    assert lib.lowbit_argmax(null, 16, 1, good, good, good, big, st) == ARG
+    assert lib.lowbit_argmax(good, 16, 0, good, good, good, big, st) == ARG
+    assert lib.lowbit_argmax(good, 0, 1, good, good, good, big, st) == SHAPE
+    assert lib.lowbit_argmax(odd, 16, 1, good, good, good, big, st) == ALIGN
+    assert lib.lowbit_argmax(good, 16, 1, good, good, good, 8, st) == WS
+    # lm head
+    assert lib.lowbit_lm_head(Q1, good, good, 16, 128, good, 9, good, good, good, good, big, st) == ARG
+    assert lib.lowbit_lm_head(Q1, good, good, 16, 128, good, 1, good, null, good, good, big, st) == ARG
+    assert lib.lowbit_lm_head(Q1, good, good, 16, 120, good, 1, good, good, good, good, big, st) == SHAPE
+    assert lib.lowbit_lm_head(Q1, good, good, 16, 128, good, 1, good, good, good, good, 8, st) == WS
