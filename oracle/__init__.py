@@ -85,6 +85,14 @@ def _load():
         lib.orc_silu.restype = ctypes.c_double
         lib.orc_ffn_hidden.argtypes = [ctypes.c_int, p, p, i64, i64, p, i64, p, p, p]
         lib.orc_ffn_hidden.restype = None
+        lib.orc_t2_quantize.argtypes = [p, i64, i64, p, p]
+        lib.orc_t2_quantize.restype = None
+        lib.orc_base3_row_bytes.argtypes = [i64]
+        lib.orc_base3_row_bytes.restype = i64
+        lib.orc_base3_pack.argtypes = [p, i64, i64, p]
+        lib.orc_base3_pack.restype = None
+        lib.orc_base3_unpack.argtypes = [p, i64, i64, p]
+        lib.orc_base3_unpack.restype = None
         _lib = lib
     return _lib
 
@@ -267,3 +275,53 @@ def ffn(fmt, gu_codes, gu_scales, dn_codes, dn_scales, k, f, x_fp16, row0=0, nro
     if z is None:
         z = ffn_hidden(fmt, gu_codes, gu_scales, k, f, x_fp16)
     return gemv(fmt, dn_codes, dn_scales, k, f, z, row0=row0, nrows=nrows)
+
+
+# --------------------------------------------------------------------------
+# ternary quantiser and base-3 storage
+#
+# [P2] "Como funciona la compresion": log2(3) bits per ternary weight plus
+# one FP16 scale per 128, ~1.71 bits per weight.  The pages give no ternary
+# rounding rule; this build reads it as s = max |w| of the group and t the
+# nearest of {-1, 0, +1} to w / s, ties to 0 (t = sign(w) iff 2|w| > s).
+
+def t2_quantize(w_fp16: np.ndarray):
+    """FP16 [n][k] -> (t int8 [n][k], s FP16 [n][k/128]) by the rule above."""
+    w = np.ascontiguousarray(w_fp16, dtype=np.uint16)
+    n, k = w.shape
+    t = np.zeros((n, k), dtype=np.int8)
+    s = np.zeros((n, k // 128), dtype=np.uint16)
+    _load().orc_t2_quantize(_ptr(w), n, k, _ptr(t), _ptr(s))
+    return t, s
+
+
+def base3_row_bytes(k: int) -> int:
+    return int(_load().orc_base3_row_bytes(k))
+
+
+def base3_pack(t: np.ndarray) -> np.ndarray:
+    """int8 t [n][k] -> uint8 [n][ceil(k/5)], five trits per byte."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    n, k = t.shape
+    out = np.zeros((n, base3_row_bytes(k)), dtype=np.uint8)
+    _load().orc_base3_pack(_ptr(t), n, k, _ptr(out))
+    return out
+
+
+def base3_unpack(b: np.ndarray, n: int, k: int) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    t = np.zeros((n, k), dtype=np.int8)
+    _load().orc_base3_unpack(_ptr(b), n, k, _ptr(t))
+    return t
+
+
+def t2_codes_to_trits(codes: np.ndarray, n: int, k: int) -> np.ndarray:
+    """The t values [n][k] held by ternary codes (layout v1), via the
+    per-weight code reader."""
+    f = _load().orc_code_value
+    c = np.ascontiguousarray(codes)
+    t = np.zeros((n, k), dtype=np.int8)
+    for r in range(n):
+        for j in range(k):
+            t[r, j] = f(T2, _ptr(c), k, r, j)
+    return t

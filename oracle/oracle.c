@@ -311,3 +311,69 @@ void orc_ffn_hidden(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scales,
       z_fp16[i * f + j] = orc_f64_to_fp16_rne(orc_silu(gate) * up);
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Ternary quantiser and base-3 storage.                                  */
+/* [P2] "Como funciona la compresion": a ternary weight carries log2(3)   */
+/* bits, ~1.71 bits per weight with one FP16 scale per 128.  The pages    */
+/* give no ternary rounding rule; the rule here is this build's reading:  */
+/* s = max |w| of the group (as the 1-bit worked example), and t is the   */
+/* nearest of {-1, 0, +1} to w / s, ties going to 0: t = sign(w) when     */
+/* 2 |w| > s (IEEE comparison in double, exact for FP16 inputs; false for */
+/* a NaN, and for 2 |w| = s), else 0.                                     */
+
+void orc_t2_quantize(const uint16_t* w, int64_t n, int64_t k, int8_t* t_out,
+                     uint16_t* s_out) {
+  int64_t groups = k / 128;
+  for (int64_t row = 0; row < n; ++row)
+    for (int64_t g = 0; g < groups; ++g) {
+      uint16_t smax = 0;
+      for (int64_t j = 0; j < 128; ++j) {
+        uint16_t m = magnitude_bits(w[row * k + g * 128 + j]);
+        if (m > smax) smax = m;
+      }
+      s_out[row * groups + g] = smax;
+      double s = orc_fp16_to_f64(smax);
+      for (int64_t j = 0; j < 128; ++j) {
+        uint16_t h = w[row * k + g * 128 + j];
+        double v = orc_fp16_to_f64(h);
+        int8_t t = 0;
+        if (2.0 * fabs(v) > s) t = (h & 0x8000) ? -1 : 1;
+        t_out[row * k + g * 128 + j] = t;
+      }
+    }
+}
+
+/* Base-3 storage: five trits per byte, byte = sum_i (t_i + 1) * 3^i for the
+ * weights 5j + i of a row (i = 0..4), rows packed one after another with
+ * ceil(k / 5) bytes each; positions past k hold t = 0.  8/5 + 16/128 =
+ * 1.725 bits per weight with the FP16 scales. */
+int64_t orc_base3_row_bytes(int64_t k) { return (k + 4) / 5; }
+
+void orc_base3_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* out) {
+  int64_t rb = orc_base3_row_bytes(k);
+  for (int64_t row = 0; row < n; ++row)
+    for (int64_t j = 0; j < rb; ++j) {
+      int v = 0, p = 1;
+      for (int i = 0; i < 5; ++i) {
+        int64_t col = 5 * j + i;
+        int tv = col < k ? t[row * k + col] : 0;
+        v += (tv + 1) * p;
+        p *= 3;
+      }
+      out[row * rb + j] = (uint8_t)v;
+    }
+}
+
+/* Inverse; a byte of 243..255 (never written by the packer) decodes with
+ * its fifth digit taken mod 3. */
+void orc_base3_unpack(const uint8_t* in, int64_t n, int64_t k, int8_t* t) {
+  int64_t rb = orc_base3_row_bytes(k);
+  for (int64_t row = 0; row < n; ++row)
+    for (int64_t col = 0; col < k; ++col) {
+      int v = in[row * rb + col / 5];
+      int i = (int)(col % 5);
+      for (int q = 0; q < i; ++q) v /= 3;
+      t[row * k + col] = (int8_t)(v % 3 - 1);
+    }
+}

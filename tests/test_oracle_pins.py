@@ -478,3 +478,88 @@ def test_ffn_closed_forms():
     gc2, gs2 = oracle.t2_pack(sw, gsw)
     assert not np.array_equal(oracle.ffn_hidden(oracle.T2, gc2, gs2, k, f, x),
                               oracle.ffn_hidden(oracle.T2, gc, gs, k, f, x))
+
+
+# --------------------------------------------------------------------------
+# ternary quantiser (rule: s = max|w|, t = sign(w) iff 2|w| > s, ties to 0)
+# and base-3 storage (five trits per byte)
+
+def test_t2_quantize_rule_exhaustive_magnitudes():
+    # every FP16 magnitude m <= S against several group maxima S, decided
+    # with exact rationals; both signs
+    mags = np.arange(0x7C01, dtype=np.uint32).astype(np.uint16)  # 0 .. +inf
+    for S in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x3C01, 0x5BFF, 0x7BFF, 0x7C00):
+        cand = mags[mags <= S]
+        sgn = (np.arange(cand.size) % 2).astype(np.uint16) << 15
+        vals = cand | sgn
+        per = 127
+        groups = (vals.size + per - 1) // per
+        w = np.zeros((groups, 128), np.uint16)
+        w[:, 0] = S  # the group maximum
+        flat = np.zeros(groups * per, np.uint16)
+        flat[:vals.size] = vals
+        w[:, 1:] = flat.reshape(groups, per)
+        t, s = oracle.t2_quantize(w.reshape(1, -1))
+        t = t.reshape(groups, 128)
+        assert (s == S).all()
+        sv = Fraction(oracle.fp16_to_f64(S)) if S != 0x7C00 else None
+        for gi in range(groups):
+            for j in range(1, 128):
+                h = int(w[gi, j])
+                m = h & 0x7FFF
+                if sv is None:  # s = inf: 2|w| > inf never holds
+                    want = 0
+                else:
+                    av = Fraction(oracle.fp16_to_f64(m)) if m != 0x7C00 else None
+                    want = 0 if (av is None or not 2 * av > sv) else (-1 if h & 0x8000 else 1)
+                assert t[gi, j] == want, (hex(S), hex(h))
+
+
+def test_t2_quantize_nearest_and_worked_group():
+    g = synth.rng(41)
+    w = synth.fp16_normal(g, (7, 384), 0.1)
+    t, s = oracle.t2_quantize(w)
+    v = w.view(np.float16).astype(np.float64)
+    sv = np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    assert np.array_equal(s, (v.reshape(7, 3, 128).__abs__().max(axis=2)).astype(np.float16).view(np.uint16))
+    # s * t is a nearest point of {-s, 0, +s} (exact in double for FP16 values)
+    d = np.stack([np.abs(v - sv * c) for c in (-1, 0, 1)])
+    assert np.all(np.abs(v - sv * t) <= d.min(axis=0))
+    # hand-built group: s = 1 (first weight), ties to 0, subnormals, -0
+    vals = [1.0, 0.5, np.nextafter(np.float16(0.5), np.float16(1)), np.nextafter(np.float16(0.5), np.float16(0)),
+            -0.75, -0.5, 0.0, -0.0, 6e-8, -1.0]
+    wg = np.zeros((1, 128), np.float16)
+    wg[0, :len(vals)] = vals
+    t1, s1 = oracle.t2_quantize(wg.view(np.uint16))
+    assert s1[0, 0] == 0x3C00
+    assert list(t1[0, :len(vals)]) == [1, 0, 1, 0, -1, 0, 0, 0, 0, -1]
+    assert not t1[0, len(vals):].any()
+    # quantise -> pack -> read codes back gives t; unpack gives s * t exactly
+    codes, scales = oracle.t2_pack(t, s)
+    assert np.array_equal(oracle.t2_codes_to_trits(codes, 7, 384), t)
+
+
+def test_base3_closed_forms_and_sizes():
+    k = 10
+    rows = np.array([[-1] * 10, [0] * 10, [1] * 10,
+                     [1, -1, -1, -1, -1, -1, 1, -1, -1, -1],
+                     [0, 0, 0, 0, 1, 1, 1, 1, 1, 1]], np.int8)
+    b = oracle.base3_pack(rows)
+    assert b.shape == (5, 2)
+    assert b.tolist() == [[0, 0], [121, 121], [242, 242], [2, 6], [202, 242]]
+    # k = 128: 25 full bytes and one holding three trits plus two padding
+    # zeros (digit 1): for an all -1 row that byte is 27 + 81 = 108
+    b128 = oracle.base3_pack(np.full((1, 128), -1, np.int8))
+    assert b128.shape == (1, 26) and b128[0, 25] == 108 and not b128[0, :25].any()
+    # round trip
+    g = synth.rng(42)
+    t = synth.ternary(g, (9, 640))
+    assert np.array_equal(oracle.base3_unpack(oracle.base3_pack(t), 9, 640), t)
+    # the pages' arithmetic: log2(3) + 16/128 ~ 1.71 bits per weight is the
+    # bound; five trits per byte gives 8/5 + 16/128 = 1.725 (0.9 % above it)
+    assert oracle.base3_row_bytes(5120) == 1024
+    bpw = 8 * oracle.base3_row_bytes(5120) / 5120 + 16 / 128
+    assert bpw == 1.725 and round(math.log2(3) + 16 / 128, 2) == 1.71
+    assert bpw / (math.log2(3) + 16 / 128) < 1.01
+    # a byte the packer never writes (243..255) decodes with its fifth digit mod 3
+    assert oracle.base3_unpack(np.array([[243]], np.uint8), 1, 5).tolist() == [[-1, -1, -1, -1, -1]]
