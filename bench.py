@@ -21,7 +21,8 @@ Printed: one JSON line with
              sweep), the decode FFN chain (gate+up GEMV, SiLU-gated
              product, down GEMV; eager and as a graph), the two ends of
              a decode step (8-row embedding gather; LM head with top-1
-             against the GEMV alone), the FP16 -> Q1
+             against the GEMV alone), the ternary quantiser and base-3
+             storage conversions, the FP16 -> Q1
              quantiser and the pp512 prefill GEMMs;
              for the GEMVs also the per-step time of a HIP graph that holds
              one step per rotated copy (small matrices are otherwise timed
@@ -288,6 +289,42 @@ def time_ends(n, k, seed):
     return out
 
 
+def time_ternary(n, k, seed, steps=10):
+    """FP16 -> ternary quantiser and the base-3 storage conversions on an
+    LM-head-sized matrix: HBM bytes moved (read + written) per second."""
+    import torch
+
+    from bit_matmul_lowbit_amd import lowbit, synth
+
+    w = synth.dev_fp16_normal((n, k), 0.02, seed)
+    codes, scales = lowbit.lowbit_quantize_t2(w)
+    b3, srm = lowbit.lowbit_t2_to_base3(codes, scales, n, k)
+    torch.cuda.synchronize()
+    cb, sb = codes.numel(), scales.numel() * 2
+    jobs = {
+        "quantize_t2": (lambda: lowbit.lowbit_quantize_t2(w, codes, scales), n * k * 2 + cb + sb),
+        "t2_to_base3": (lambda: lowbit.lowbit_t2_to_base3(codes, scales, n, k, b3, srm),
+                        cb + sb + b3.numel() + srm.numel() * 2),
+        "base3_to_t2": (lambda: lowbit.lowbit_base3_to_t2(b3, srm, n, k, codes, scales),
+                        b3.numel() + srm.numel() * 2 + cb + sb),
+    }
+    out = {"base3_bits_per_weight": round(8 * b3.numel() / (n * k) + 16 / 128, 4)}
+    for name, (fn, moved) in jobs.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        out[name] = {"us": round(ms * 1e3, 1), "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
+    del w, codes, scales, b3, srm
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_quantize(n, k, seed, steps, warmup):
     import torch
 
@@ -522,6 +559,8 @@ def main():
                 "ffn_t2_1p7b_k2048_f6144_b1": ("t2", 2048, 6144, 1)}.items():
             sec[key] = time_ffn(ff, kf, fff, bf, 1100 + fff + bf, 30, 5)
             log(f"[bench] {key}: {sec[key]}")
+        sec["ternary_151936x5120"] = time_ternary(151936, 5120, 1950)
+        log(f"[bench] ternary_151936x5120: {sec['ternary_151936x5120']}")
         sec["ends_t2_151936x5120_b1"] = time_ends(151936, 5120, 1900)
         log(f"[bench] ends_t2_151936x5120_b1: {sec['ends_t2_151936x5120_b1']}")
         for key, (f2, m2, n2, k2) in {"gemm_pp512_t2_512x6144x2048": ("t2", 512, 6144, 2048),

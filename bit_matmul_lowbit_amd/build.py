@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblowbit.so")
-SOURCES = ["lowbit_api.cpp", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "ffn.hip", "ends.hip"]
+SOURCES = ["lowbit_api.cpp", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "ffn.hip", "ends.hip", "ternary.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -25,6 +25,13 @@ hipError_t launch_pack_t2(const int8_t* t, const uint16_t* s, int64_t n, int64_t
                           uint8_t* codes, uint16_t* scales, hipStream_t st);
 hipError_t launch_unpack(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                          int64_t k, uint16_t* w, hipStream_t st);
+// ternary quantiser and base-3 storage
+hipError_t launch_quantize_t2(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                              uint16_t* scales, hipStream_t st);
+hipError_t launch_t2_to_base3(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                              uint8_t* out, uint16_t* out_scales, hipStream_t st);
+hipError_t launch_base3_to_t2(const uint8_t* in, const uint16_t* in_scales, int64_t n, int64_t k,
+                              uint8_t* codes, uint16_t* scales, hipStream_t st);
 
 // decode GEMV: subset-sum tables for b < kMfmaMinBatch, matrix cores above
 constexpr int kMfmaMinBatch = 3;

@@ -251,4 +251,40 @@ int lowbit_lm_head(int fmt, const void* codes, const uint16_t* scales, int64_t n
                                            stream));
 }
 
+int lowbit_quantize_t2(const uint16_t* w_fp16, int64_t n, int64_t k, void* codes,
+                       uint16_t* scales, hipStream_t stream) {
+  if (!w_fp16 || !codes || !scales) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(w_fp16) || !aligned16(codes) || !aligned16(scales)) return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_quantize_t2(w_fp16, n, k, static_cast<uint8_t*>(codes),
+                                               scales, stream));
+}
+
+size_t lowbit_base3_bytes(int64_t n, int64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  return (size_t)(n * ((k + 4) / 5));
+}
+
+int lowbit_t2_to_base3(const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                       uint8_t* base3_out, uint16_t* scales_out, hipStream_t stream) {
+  if (!codes || !scales || !base3_out || !scales_out) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1u) ||
+      (reinterpret_cast<uintptr_t>(scales_out) & 1u))
+    return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_t2_to_base3(static_cast<const uint8_t*>(codes), scales, n, k,
+                                               base3_out, scales_out, stream));
+}
+
+int lowbit_base3_to_t2(const uint8_t* base3, const uint16_t* scales_rm, int64_t n, int64_t k,
+                       void* codes, uint16_t* scales, hipStream_t stream) {
+  if (!base3 || !scales_rm || !codes || !scales) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1u) ||
+      (reinterpret_cast<uintptr_t>(scales_rm) & 1u))
+    return LOWBIT_ERR_ALIGN;
+  return hip_status(lowbit::launch_base3_to_t2(base3, scales_rm, n, k,
+                                               static_cast<uint8_t*>(codes), scales, stream));
+}
+
 }  // extern "C"

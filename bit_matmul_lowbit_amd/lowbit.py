@@ -23,6 +23,7 @@ FORMATS = {"q1": LOWBIT_FMT_Q1_G128, "t2": LOWBIT_FMT_T2_G128}
 SYMBOLS = [
     "lowbit_version", "lowbit_status_str", "lowbit_codes_bytes", "lowbit_scales_bytes",
     "lowbit_quantize_q1", "lowbit_pack_t2", "lowbit_pack", "lowbit_unpack",
+    "lowbit_quantize_t2", "lowbit_base3_bytes", "lowbit_t2_to_base3", "lowbit_base3_to_t2",
     "lowbit_gemv_workspace_bytes", "lowbit_gemv_prepare", "lowbit_gemv_accumulate",
     "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32", "lowbit_silu_mul",
     "lowbit_ffn_workspace_bytes", "lowbit_ffn", "lowbit_embed", "lowbit_argmax_workspace_bytes",
@@ -73,6 +74,10 @@ def load() -> ctypes.CDLL:
         "lowbit_argmax": ([p, i64, i64, p, p, p, sz, p], i),
         "lowbit_lm_head_workspace_bytes": ([i, i64, i64, i64], sz),
         "lowbit_lm_head": ([i, p, p, i64, i64, p, i64, p, p, p, p, sz, p], i),
+        "lowbit_quantize_t2": ([p, i64, i64, p, p, p], i),
+        "lowbit_base3_bytes": ([i64, i64], sz),
+        "lowbit_t2_to_base3": ([p, p, i64, i64, p, p, p], i),
+        "lowbit_base3_to_t2": ([p, p, i64, i64, p, p, p], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -385,3 +390,45 @@ def lowbit_lm_head(fmt, codes, scales, n: int, k: int, x, out=None, idx=None, va
                                  _dev(workspace, (torch.uint8,), "workspace"), workspace.numel(),
                                  _stream(stream)), "lowbit_lm_head")
     return out, idx, val
+
+
+def lowbit_quantize_t2(w, codes=None, scales=None, stream=None):
+    """FP16 [n][k] -> ternary g128 codes and scales (layout v1)."""
+    import torch
+
+    n, k = w.shape
+    codes, scales = _planes("t2", n, k, w.device, codes, scales)
+    _check(load().lowbit_quantize_t2(_dev(w, (torch.float16,), "w"), n, k,
+                                     _dev(codes, (torch.uint8,), "codes"),
+                                     _dev(scales, (torch.float16, torch.int16), "scales"),
+                                     _stream(stream)), "lowbit_quantize_t2")
+    return codes, scales
+
+
+def lowbit_t2_to_base3(codes, scales, n: int, k: int, out=None, out_scales=None, stream=None):
+    """Ternary codes -> (base-3 bytes [n][ceil(k/5)], scales FP16 [n][k/128])."""
+    import torch
+
+    if out is None:
+        out = torch.empty((n, (k + 4) // 5), dtype=torch.uint8, device=codes.device)
+    if out_scales is None:
+        out_scales = torch.empty((n, k // 128), dtype=torch.float16, device=codes.device)
+    _check(load().lowbit_t2_to_base3(_dev(codes, (torch.uint8,), "codes"),
+                                     _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                                     _dev(out, (torch.uint8,), "out"),
+                                     _dev(out_scales, (torch.float16, torch.int16), "out_scales"),
+                                     _stream(stream)), "lowbit_t2_to_base3")
+    return out, out_scales
+
+
+def lowbit_base3_to_t2(b3, scales_rm, n: int, k: int, codes=None, scales=None, stream=None):
+    """Base-3 bytes + row-major scales -> ternary codes and scales (layout v1)."""
+    import torch
+
+    codes, scales = _planes("t2", n, k, b3.device, codes, scales)
+    _check(load().lowbit_base3_to_t2(_dev(b3, (torch.uint8,), "b3"),
+                                     _dev(scales_rm, (torch.float16, torch.int16), "scales_rm"),
+                                     n, k, _dev(codes, (torch.uint8,), "codes"),
+                                     _dev(scales, (torch.float16, torch.int16), "scales"),
+                                     _stream(stream)), "lowbit_base3_to_t2")
+    return codes, scales

@@ -153,6 +153,33 @@ int lowbit_pack(int fmt, const void* src, const uint16_t* src_scales,
 int lowbit_unpack(int fmt, const void* codes, const uint16_t* scales,
                   int64_t n, int64_t k, uint16_t* w_fp16, hipStream_t stream);
 
+/* Ternary quantiser  [P2 "Como funciona la compresion": w = s t, t in
+ * {-1, 0, +1}, one FP16 scale per 128].  The pages give no rounding rule;
+ * this library's: s = max |w| of each group of 128 (as the 1-bit worked
+ * example), and t = sign(w) if 2|w| > s, else 0 -- the nearest of
+ * {-1, 0, +1} to w / s, ties to 0 (a NaN weight, or a group whose maximum
+ * is NaN or infinite, gives t = 0 except for 2|w| > s).
+ *   w_fp16 : [n][k] row-major FP16 (device, read-only)
+ *   codes  : lowbit_codes_bytes(T2, n, k) bytes, scales : [padded n][k/128]
+ *            (device, written; layout v1, as lowbit_pack_t2 writes them). */
+int lowbit_quantize_t2(const uint16_t* w_fp16, int64_t n, int64_t k, void* codes,
+                       uint16_t* scales, hipStream_t stream);
+
+/* Base-3 storage of ternary codes  [P2: log2(3) + 16/128 ~ 1.71 bits per
+ * weight is the bound]: five trits per byte, byte = sum_i (t_i + 1) 3^i
+ * for the weights 5j + i of a row, ceil(k/5) bytes per row, rows one after
+ * another, positions past k holding t = 0; scales row-major [n][k/128].
+ * 8/5 + 16/128 = 1.725 bits per weight.  A storage format: the GEMV and
+ * GEMM read the two-plane codes, to and from which these calls convert. */
+size_t lowbit_base3_bytes(int64_t n, int64_t k);   /* n * ceil(k/5); 0 on a bad shape */
+int lowbit_t2_to_base3(const void* codes, const uint16_t* scales, int64_t n, int64_t k,
+                       uint8_t* base3_out, uint16_t* scales_out, hipStream_t stream);
+/* Inverse; a byte of 243..255 (never written above) decodes with its fifth
+ * digit taken mod 3.  Rows of the last tile past n get zero codes and
+ * scales. */
+int lowbit_base3_to_t2(const uint8_t* base3, const uint16_t* scales_rm, int64_t n, int64_t k,
+                       void* codes, uint16_t* scales, hipStream_t stream);
+
 /* Workspace bytes lowbit_gemv needs for (fmt, n, k, b); 0 on a bad shape. */
 size_t lowbit_gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b);
 

@@ -192,3 +192,18 @@ def test_ends_of_step_queries_and_validation(lib):
     assert lib.lowbit_lm_head(Q1, good, good, 16, 128, good, 1, good, null, good, good, big, st) == ARG
     assert lib.lowbit_lm_head(Q1, good, good, 16, 120, good, 1, good, good, good, good, big, st) == SHAPE
     assert lib.lowbit_lm_head(Q1, good, good, 16, 128, good, 1, good, good, good, good, 8, st) == WS
+
+
+def test_ternary_storage_queries_and_validation(lib):
+    assert lowbit.load().lowbit_base3_bytes(151936, 5120) == 151936 * 1024
+    assert lowbit.load().lowbit_base3_bytes(3, 128) == 3 * 26
+    assert lowbit.load().lowbit_base3_bytes(3, 100) == 0
+    good, bad_align, null, st, odd = P(0x10000), P(0x10008), P(0), P(0), P(0x10001)
+    assert lib.lowbit_quantize_t2(null, 16, 128, good, good, st) == ARG
+    assert lib.lowbit_quantize_t2(good, 16, 120, good, good, st) == SHAPE
+    assert lib.lowbit_quantize_t2(good, 16, 128, bad_align, good, st) == ALIGN
+    assert lib.lowbit_t2_to_base3(good, good, 16, 128, null, good, st) == ARG
+    assert lib.lowbit_t2_to_base3(good, odd, 16, 128, good, good, st) == ALIGN
+    assert lib.lowbit_t2_to_base3(good, good, 0, 128, good, good, st) == SHAPE
+    assert lib.lowbit_base3_to_t2(good, good, 16, 128, bad_align, good, st) == ALIGN
+    assert lib.lowbit_base3_to_t2(good, good, 16, 130, good, good, st) == SHAPE
