@@ -29,11 +29,16 @@ T2 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# tests/test_oracle_mutations.py points this at deliberately broken builds
+# of oracle.c to show that the pins catch each mistake
+_OVERRIDE = os.environ.get("LOWBIT_ORACLE_LIB_OVERRIDE")
+_LIB = _OVERRIDE or os.path.join(_HERE, "liboracle.so")
 
 
 def build(force: bool = False) -> str:
     """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math)."""
+    if _OVERRIDE:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.run(
