@@ -17,6 +17,15 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<1> { static constexpr int cell_bytes = 16; };
 template <> struct Fmt<2> { static constexpr int cell_bytes = 32; };
 
+// y[0 .. count) = 0 by the threads gid = 0, stride, 2 stride, ... of a grid:
+// 16-byte stores (y is 16-byte aligned), then the count % 4 tail.
+__device__ __forceinline__ void zero_f32(float* y, int64_t count, int64_t gid, int64_t stride) {
+  const int64_t nv = count / 4;
+  for (int64_t i = gid; i < nv; i += stride)
+    reinterpret_cast<float4*>(y)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (gid < count - nv * 4) y[nv * 4 + gid] = 0.0f;
+}
+
 // Kernel launchers (host side, defined in the .hip files).  All return a
 // hipError_t from the launch; shapes were validated by the caller.
 hipError_t launch_quantize_q1(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,

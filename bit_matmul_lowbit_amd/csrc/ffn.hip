@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
                                                        int64_t ycount) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = gid; i < ycount; i += stride) y[i] = 0.0f;
+  zero_f32(y, ycount, gid, stride);
   const int64_t cpr = f / 8;  // 16-byte vectors per batch row
   for (int64_t i = gid; i < nvec; i += stride) {
     int row;
@@ -84,7 +84,7 @@ int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 hipError_t launch_silu(const float* h, int64_t f, int64_t b, void* z, bool mfma, float* y,
                        int64_t ycount, hipStream_t st) {
   const int64_t nvec = mfma ? (f / kGroup) * 4 * 64 : b * f / 8;
-  const int64_t work = nvec > ycount ? nvec : ycount;
+  const int64_t work = nvec > (ycount + 3) / 4 ? nvec : (ycount + 3) / 4;
   int64_t blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;

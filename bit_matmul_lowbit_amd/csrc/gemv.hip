@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kWG) void gemv_prepare_kernel(const uint4* __restri
                                                            int64_t ycount) {
   const int64_t gid = (int64_t)blockIdx.x * kWG + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kWG;
-  for (int64_t i = gid; i < ycount; i += stride) y[i] = 0.0f;
+  zero_f32(y, ycount, gid, stride);
   for (int64_t i = gid; i < nvec; i += stride) xs[i] = x[i];
 }
 
@@ -487,9 +487,10 @@ hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t 
                                void* ws, hipStream_t st) {
   if (b >= kMfmaMinBatch) return launch_gemv_mfma_prepare(n, k, x, b, y, ws, st);
   const int64_t nvec = b * k / 8;  // 16-byte vectors of x (k % 128 == 0)
-  const int64_t work = nvec > n * b ? nvec : n * b;
+  const int64_t yvec = (n * b + 3) / 4;  // y is zeroed 16 bytes at a time
+  const int64_t work = nvec > yvec ? nvec : yvec;
   int64_t blocks = (work + kWG - 1) / kWG;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(gemv_prepare_kernel, dim3((unsigned)blocks), dim3(kWG), 0, st,
                      reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b);
   return hipGetLastError();

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_prepare_kernel(const uint16_t* 
                                                                 int64_t ycount) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = gid; i < ycount; i += stride) y[i] = 0.0f;
+  zero_f32(y, ycount, gid, stride);
   for (int64_t i = gid; i < nvec; i += stride) {
     // vector i = (group g, step j, lane l): batch row l % 16, chunk 16 g + 4 (l / 16) + j
     const int l = (int)(i & 63);
@@ -307,9 +307,10 @@ int64_t gemv_mfma_workspace_bytes(int64_t k) { return (k / kGroup) * kSteps * kX
 hipError_t launch_gemv_mfma_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                     void* ws, hipStream_t st) {
   const int64_t nvec = (k / kGroup) * kSteps * 64;
-  const int64_t work = nvec > n * b ? nvec : n * b;
+  const int64_t yvec = (n * b + 3) / 4;
+  const int64_t work = nvec > yvec ? nvec : yvec;
   int64_t blocks = (work + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(gemv_mfma_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, k,
                      (int)b, static_cast<uint4*>(ws), nvec, y, n * b);
   return hipGetLastError();
