@@ -6,15 +6,16 @@
 // [P1] 7minutos.es tutorial, section 7: bit 0 -> -s, bit 1 -> +s.
 // [P2] "Como funciona la compresion": w = s * t, t in {-1, 0, +1}.
 //
-// Tiling: a 256-thread work-group owns a BM x BN output tile (128 x 128 or
-// 64 x 64); its 4 waves form a 2 x 2 grid of (BM/2) x (BN/2) wave tiles made
-// of 32x32 blocks of the 32x32x16 BF16 matrix-core instruction.  The K loop
-// steps one scale group (128) at a time through double-buffered LDS:
+// Tiling: a team of WM x WN waves owns a BM x BN output tile (128 x 128 and
+// 64 x 64 with 2 x 2 waves, 128 x 96 with 4 x 3); each wave's tile is made of
+// 32x32 blocks of the 32x32x16 BF16 matrix-core instruction.  The K loop
+// steps one scale group (128) at a time through LDS:
 //   * X[BM][128] BF16, the codes of W[BN][128] and the scales are loaded
-//     into registers one group ahead; after the current group's MFMAs are
-//     issued they are written to the other LDS buffer, the codes expanded to
-//     exact BF16 {-1, 0, +1}.  The scale is NOT folded in: a BF16 scale
-//     would lose 3 of FP16's 11 significant bits;
+//     into registers groups ahead and written to LDS while the matrix cores
+//     work (a second LDS buffer for 128 x 128 tiles; one buffer and a
+//     three-stage register ring when each wave holds one 32 x 32 block), the
+//     codes expanded to exact BF16 {-1, 0, +1}.  The scale is NOT folded in:
+//     a BF16 scale would lose 3 of FP16's 11 significant bits;
 //   * 8 k-steps of 16 accumulate the group's unscaled FP32 partial C_g, then
 //     C += s[n][g] * C_g in FP32 (one FMA per accumulator).
 // LDS rows are 256 B whose 16-byte slots are XOR-swizzled by the row index, so
@@ -94,47 +95,60 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// 64 x 64 tiles keep a single LDS buffer per team (3 waves per SIMD fit);
-// larger tiles double-buffer
-template <int BM, int BN>
-constexpr bool kSingleBuffer = BM * BN == 64 * 64;
+// Waves with a single 32 x 32 block keep a single LDS buffer per team (three
+// waves per SIMD fit); larger wave blocks double-buffer
+template <int BM, int BN, int WM, int WN>
+constexpr bool kSingleBuffer = BM == 32 * WM && BN == 32 * WN;
 
-template <int FMT, bool OUT_F32, int BM, int BN, int KT>
-__global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) void gemm_kernel(
+// A team of WM x WN waves owns a BM x BN tile (wave tiles (BM/WM) x (BN/WN),
+// made of 32 x 32 blocks); KT teams split the tile's K groups.
+template <int FMT, bool OUT_F32, int BM, int BN, int KT, int WM = 2, int WN = 2>
+__global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ? 2 : 1)) void gemm_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y) {
-  constexpr int WBM = BM / 64;                    // 32-row blocks per wave
-  constexpr int WBN = BN / 64;                    // 32-col blocks per wave
-  constexpr int XL = BM * kRowU4 / kThreads;      // 16-B X slots per thread per group
+  constexpr int NT = 64 * WM * WN;                // threads per team
+  constexpr int WBM = BM / (32 * WM);             // 32-row blocks per wave
+  constexpr int WBN = BN / (32 * WN);             // 32-col blocks per wave
+  constexpr int XS = BM * kRowU4;                 // 16-B X slots per group
+  constexpr int XL = (XS + NT - 1) / NT;          // X slots per thread per group
+  constexpr bool kXPartial = XS % NT != 0;        // the last slot is not every thread's
   constexpr int CB = Fmt<FMT>::cell_bytes;
-  constexpr int RPT = BN / 16;                    // W rows expanded per thread per group
-  constexpr int TPC = 16 / RPT;                   // threads per code cell
+  constexpr int TPC = NT / BN;                    // threads per code cell
+  constexpr int RPT = 16 / TPC;                   // W rows expanded per thread per group
+  static_assert(NT % BN == 0 && 16 % TPC == 0 && RPT <= 8, "W cells split evenly");
+  static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tiles of 32 x 32 blocks");
 
-  constexpr bool kSingle = kSingleBuffer<BM, BN>;
+  constexpr bool kSingle = kSingleBuffer<BM, BN, WM, WN>;
   constexpr int NB = kSingle ? 1 : 2;  // LDS buffers per team
   __shared__ uint4 xs[KT][NB][BM * kRowU4];
   __shared__ uint4 ws[KT][NB][BN * kRowU4];
 
-  // KT teams of 256 threads share the output tile; team t takes the groups
+  // KT teams of NT threads share the output tile; team t takes the groups
   // g = t (mod KT) and has its own LDS buffers
-  const int tid = threadIdx.x & (kThreads - 1);
-  const int team = KT == 1 ? 0 : (int)(threadIdx.x / kThreads);
+  const int tid = (NT & (NT - 1)) == 0 ? (int)(threadIdx.x & (NT - 1))
+                  : KT == 1             ? (int)threadIdx.x
+                                        : (int)(threadIdx.x % NT);
+  const int team = KT == 1 ? 0 : (int)(threadIdx.x / NT);
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t groups = k / BK;
   const int64_t chunks = k / kChunk;
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
 
-  // --- X staging: slot i = tid + 256*j is row i/16, 16-byte column i%16 of
+  // --- X staging: slot i = tid + NT*j is row i/16, 16-byte column i%16 of
   // the group; rows past m read row m-1 (those outputs are never stored).
+  // When NT does not divide the slots, the last slot exists for the first
+  // XS - NT*(XL-1) threads only (whole waves): the others load a valid row
+  // and store nothing.
   const uint16_t* xsrc[XL];
   int xdst[XL];
+  const bool xlast = !kXPartial || tid + NT * (XL - 1) < XS;
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
-    const int i = tid + kThreads * j;
+    const int i = (j == XL - 1 && !xlast) ? tid : tid + NT * j;
     int64_t row = m0 + (i >> 4);
     if (row >= m) row = m - 1;
     xsrc[j] = x + row * k + (i & 15) * 8;
@@ -144,7 +158,6 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
   // --- W codes: thread -> cell ci = tid % BN (row tile ci/16, chunk ci%16
   // of the group), rows part*RPT .. part*RPT + RPT-1 of that cell, part =
   // tid / BN; eight consecutive lanes write one row, eight different slots
-  static_assert(kThreads / TPC == BN, "one thread per cell and part");
   const int ci = tid % BN, part = tid / BN;
   const int wt = ci >> 4, wc = ci & 15;
   const int64_t gtile = n0 / kTileRows + wt;
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
   const uint16_t* sptr[WBN];
 #pragma unroll
   for (int bj = 0; bj < WBN; ++bj) {
-    ncol[bj] = n0 + wn * (BN / 2) + bj * 32 + jl;
+    ncol[bj] = n0 + wn * (BN / WN) + bj * 32 + jl;
     nvalid[bj] = ncol[bj] < n;
     const int64_t nn = nvalid[bj] ? ncol[bj] : 0;
     sptr[bj] = scales + ((nn >> 4) * groups) * kTileRows + (nn & 15);
@@ -189,6 +202,9 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
         st.q[0] = c2.x;
         st.q[1] = c2.y;
       }
+    } else if constexpr (RPT == 2) {
+      st.p[0] = *reinterpret_cast<const uint16_t*>(cell);
+      if constexpr (FMT == 2) st.q[0] = *reinterpret_cast<const uint16_t*>(cell + 16);
     } else {
       st.p[0] = *reinterpret_cast<const uint32_t*>(cell);
       if constexpr (FMT == 2) st.q[0] = *reinterpret_cast<const uint32_t*>(cell + 16);
@@ -198,7 +214,9 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
   };
   auto stash = [&](const Stage& st, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) xs[team][b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
+    for (int j = 0; j < XL; ++j)
+      if (j < XL - 1 || xlast)
+        xs[team][b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       // codes of a tile past the end are replaced by zeros (Q1: -1, never
@@ -253,10 +271,10 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
   // (even and odd k-steps), so consecutive MFMAs do not wait on each other
   constexpr int NCH = (WBM * WBN == 1 && !kSingle) ? 2 : 1;
   auto read_a = [&](int b, int step, int bi) __attribute__((always_inline)) {
-    return __builtin_bit_cast(bf16x8, xs[team][b][slot(wm * (BM / 2) + bi * 32 + jl, step * 2 + kh)]);
+    return __builtin_bit_cast(bf16x8, xs[team][b][slot(wm * (BM / WM) + bi * 32 + jl, step * 2 + kh)]);
   };
   auto read_b = [&](int b, int step, int bj) __attribute__((always_inline)) {
-    return __builtin_bit_cast(bf16x8, ws[team][b][slot(wn * (BN / 2) + bj * 32 + jl, step * 2 + kh)]);
+    return __builtin_bit_cast(bf16x8, ws[team][b][slot(wn * (BN / WN) + bj * 32 + jl, step * 2 + kh)]);
   };
   auto mfma_step = [&](f32x16 (&cg)[NCH][WBM][WBN], int step, const bf16x8 (&a)[WBM],
                        const bf16x8 (&bb)[WBN]) __attribute__((always_inline)) {
@@ -300,7 +318,10 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
 #pragma unroll
     for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(s0, bj);
     __syncthreads();
-    constexpr int kValu = FMT == 1 ? 10 : 21;  // staging VALU per MFMA of the second half
+    // staging VALU per MFMA of the second half (about 10 (Q1) / 21 (T2) per
+    // expanded W row)
+    constexpr int kValu = (RPT * (FMT == 1 ? 10 : 21) + 3) / 4;
+    constexpr int kDsw = (XL + RPT + 3) / 4;  // staging LDS writes per MFMA
 #define LOWBIT_GEMM_ITER1(G, FAR, NEAR)                                                        \
   {                                                                                           \
     fetch(gof((G) + 2), FAR);                                                                 \
@@ -329,7 +350,7 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
     _Pragma("unroll") for (int r = 0; r < 4 * WBM * WBN; ++r) {                               \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
       __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                                  \
-      __builtin_amdgcn_sched_group_barrier(0x200, (XL + RPT) / 4, 0);                         \
+      __builtin_amdgcn_sched_group_barrier(0x200, kDsw, 0);                                   \
     }                                                                                         \
     scale_add(cg, sv, (G) * KT + team < groups);                                              \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
@@ -379,9 +400,9 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
       bf16x8 a[RS][WBM], bb[RS][WBN];                                                         \
       _Pragma("unroll") for (int r = 0; r < RS; ++r) {                                        \
         _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = __builtin_bit_cast(     \
-            bf16x8, xs[team][B][slot(wm * (BM / 2) + bi * 32 + jl, (s0 + r) * 2 + kh)]);            \
+            bf16x8, xs[team][B][slot(wm * (BM / WM) + bi * 32 + jl, (s0 + r) * 2 + kh)]);           \
         _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = __builtin_bit_cast(    \
-            bf16x8, ws[team][B][slot(wn * (BN / 2) + bj * 32 + jl, (s0 + r) * 2 + kh)]);            \
+            bf16x8, ws[team][B][slot(wn * (BN / WN) + bj * 32 + jl, (s0 + r) * 2 + kh)]);           \
       }                                                                                       \
       __builtin_amdgcn_sched_barrier(0);                                                      \
       _Pragma("unroll") for (int r = 0; r < RS; ++r)                                          \
@@ -444,7 +465,7 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
 #pragma unroll
         for (int bj = 0; bj < WBN; ++bj)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) red[((bi * WBN + bj) * 16 + v) * kThreads + tid] = acc[bi][bj][v];
+          for (int v = 0; v < 16; ++v) red[((bi * WBN + bj) * 16 + v) * NT + tid] = acc[bi][bj][v];
     }
     __syncthreads();
     if (team > 0) return;
@@ -456,7 +477,7 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
 #pragma unroll
         for (int bj = 0; bj < WBN; ++bj)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[bi][bj][v] += red[((bi * WBN + bj) * 16 + v) * kThreads + tid];
+          for (int v = 0; v < 16; ++v) acc[bi][bj][v] += red[((bi * WBN + bj) * 16 + v) * NT + tid];
     }
   }
 
@@ -471,7 +492,7 @@ __global__ __launch_bounds__(kThreads * KT, (kSingleBuffer<BM, BN> ? 2 : 1)) voi
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = 8 * (v >> 2) + 4 * kh + (v & 3);
-        const int64_t mm = m0 + wm * (BM / 2) + bi * 32 + i;
+        const int64_t mm = m0 + wm * (BM / WM) + bi * 32 + i;
         if (mm >= m) continue;
         if constexpr (OUT_F32)
           static_cast<float*>(y)[mm * n + nn] = acc[bi][bj][v];
@@ -494,16 +515,17 @@ int cu_count_gemm() {
   return cached[dev];
 }
 
-template <int FMT, int BM, int BN, int KT>
+template <int FMT, int BM, int BN, int KT, int WM = 2, int WN = 2>
 hipError_t launch_tile(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                        const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
   const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+  const dim3 block(64 * WM * WN * KT);
   if (out_f32)
-    hipLaunchKernelGGL((gemm_kernel<FMT, true, BM, BN, KT>), grid, dim3(kThreads * KT), 0, st,
-                       codes, scales, x, m, n, k, y);
+    hipLaunchKernelGGL((gemm_kernel<FMT, true, BM, BN, KT, WM, WN>), grid, block, 0, st, codes,
+                       scales, x, m, n, k, y);
   else
-    hipLaunchKernelGGL((gemm_kernel<FMT, false, BM, BN, KT>), grid, dim3(kThreads * KT), 0, st,
-                       codes, scales, x, m, n, k, y);
+    hipLaunchKernelGGL((gemm_kernel<FMT, false, BM, BN, KT, WM, WN>), grid, block, 0, st, codes,
+                       scales, x, m, n, k, y);
   return hipGetLastError();
 }
 
@@ -515,6 +537,14 @@ hipError_t launch_fmt(const uint8_t* codes, const uint16_t* scales, int64_t n, i
   const int64_t big = ((n + 127) / 128) * ((m + 127) / 128);
   if (big >= 2 * (int64_t)cu_count_gemm())
     return launch_tile<FMT, 128, 128, 1>(codes, scales, n, k, x, m, y, out_f32, st);
+  // 128 x 96 tiles of twelve 32 x 32 waves (one work-group per CU, three
+  // waves per SIMD) when they fill whole rounds of the CUs: each W row is
+  // expanded once per 128 rows of X instead of 64, and a tile re-reads less
+  // from LDS per MFMA than four 64 x 64 ones
+  const int64_t cus = (int64_t)cu_count_gemm();
+  const int64_t t96 = ((n + 95) / 96) * ((m + 127) / 128);
+  if (m >= 128 && t96 >= cus && t96 % cus == 0)
+    return launch_tile<FMT, 128, 96, 1, 4, 3>(codes, scales, n, k, x, m, y, out_f32, st);
   // with no more 64 x 64 tiles than CUs, two K-teams per tile (one 8-wave
   // work-group per CU) keep twice as many waves busy
   const int64_t small = ((n + 63) / 64) * ((m + 63) / 64);

@@ -103,6 +103,28 @@ def test_one_hot_rows_read_weights_exactly(fmt):
     assert np.array_equal(yf.astype(np.float64), dense[:, cols].T)
 
 
+# Ragged shapes that reach each tile configuration of the launcher on a
+# 256-CU part: 64 x 64 tiles, one team (600 x 2000); 128 x 96 tiles filling
+# whole rounds of the CUs (500 x 6100: 64 x 4 = 256 tiles, last tile 52
+# columns and 116 rows); 128 x 128 tiles (2100 x 4100: 561 tiles).  Smaller
+# shapes above take 64 x 64 tiles with two K-teams.
+CONFIG_SHAPES = [(600, 2000, 384), (500, 6100, 256), (2100, 4100, 128)]
+
+
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("m,n,k", CONFIG_SHAPES)
+def test_tile_configs(fmt, m, n, k):
+    say(f"gemm config {fmt} m={m} n={n} k={k}")
+    g, codes, scales = _make(fmt, n, k, 960 + m + n + k)
+    x = synth.bf16_normal(g, (m, k))
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.gemm(f, codes, scales, n, k, x)
+    yf, yb = _run(fmt, codes, scales, n, k, x)
+    assert_close(yf, ref, f"gemm f32 {fmt} {m}x{n}x{k}")
+    assert np.array_equal(yb, _rne_f32_to_bf16(yf))
+    assert _bf16_ulp_ok(yb, ref)
+
+
 FULL = [("t2", 512, 6144, 2048), ("q1", 512, 2048, 6144)]
 
 
