@@ -311,13 +311,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     // k-steps run.  Stages are separate variables and the body is written out
     // three times, so no stage is indexed at run time.
     Stage s0, s1, s2;
-    fetch(gof(0), s0);
-    fetch(gof(1), s1);
-    stash(s0, 0);
     float sv[WBN];
-#pragma unroll
-    for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(s0, bj);
-    __syncthreads();
     // staging VALU per MFMA of the second half (about 10 (Q1) / 21 (T2) per
     // expanded W row)
     constexpr int kValu = (RPT * (FMT == 1 ? 10 : 21) + 3) / 4;
@@ -356,14 +350,41 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
     __syncthreads();                                                                          \
   }
+#define LOWBIT_GEMM_START1(FIRST, SECOND)                                                      \
+  {                                                                                           \
+    fetch(gof(0), FIRST);                                                                     \
+    fetch(gof(1), SECOND);                                                                    \
+    stash(FIRST, 0);                                                                          \
+    _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(FIRST, bj);          \
+    __syncthreads();                                                                          \
+  }
+    // The loop body is entered with group g in LDS and group g + 1 in s1.
+    // When the group count is not a multiple of three, the first one or two
+    // groups run before the loop with the stages named so that they leave
+    // exactly that state: no group body runs past the end (a group past the
+    // end of one K-team still runs as a no-op).  The 2 x 2 wave kernels keep
+    // the plain loop, whose last pass may run up to two bodies as no-ops:
+    // the extra entry code would cost them their third wave per SIMD.
+    constexpr bool kPeel = WM * WN > 4;
+    const int64_t rem = kPeel ? nloc % 3 : 0;
+    if (rem == 0) {
+      LOWBIT_GEMM_START1(s0, s1)
+    } else if (rem == 1) {
+      LOWBIT_GEMM_START1(s2, s0)
+      LOWBIT_GEMM_ITER1(0, s1, s0)
+    } else {
+      LOWBIT_GEMM_START1(s1, s2)
+      LOWBIT_GEMM_ITER1(0, s0, s2)
+      LOWBIT_GEMM_ITER1(1, s1, s0)
+    }
     // Branch-free body (a branch would let the compiler sink the prefetch
-    // loads into the blocks that consume them); groups past the end run as
-    // no-ops.
-    for (int64_t g = 0; g < nloc; g += 3) {
+    // loads into the blocks that consume them).
+    for (int64_t g = rem; g < nloc; g += 3) {
       LOWBIT_GEMM_ITER1(g, s2, s1)
       LOWBIT_GEMM_ITER1(g + 1, s0, s2)
       LOWBIT_GEMM_ITER1(g + 2, s1, s0)
     }
+#undef LOWBIT_GEMM_START1
 #undef LOWBIT_GEMM_ITER1
   } else {
   // Ring of four register stages: group g + 3 is fetched while group g is

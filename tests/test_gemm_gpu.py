@@ -106,9 +106,12 @@ def test_one_hot_rows_read_weights_exactly(fmt):
 # Ragged shapes that reach each tile configuration of the launcher on a
 # 256-CU part: 64 x 64 tiles, one team (600 x 2000); 128 x 96 tiles filling
 # whole rounds of the CUs (500 x 6100: 64 x 4 = 256 tiles, last tile 52
-# columns and 116 rows); 128 x 128 tiles (2100 x 4100: 561 tiles).  Smaller
-# shapes above take 64 x 64 tiles with two K-teams.
-CONFIG_SHAPES = [(600, 2000, 384), (500, 6100, 256), (2100, 4100, 128)]
+# columns and 116 rows; 450 x 6144: 4 x 64 tiles), with 1, 2 and 3 K-groups
+# (the group count mod 3 picks how the three-stage ring starts); 128 x 128
+# tiles (2100 x 4100: 561 tiles).  Smaller shapes above take 64 x 64 tiles
+# with two K-teams.
+CONFIG_SHAPES = [(600, 2000, 384), (450, 6144, 128), (500, 6100, 256), (500, 6100, 384),
+                 (2100, 4100, 128)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
