@@ -346,7 +346,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
       __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                                  \
       __builtin_amdgcn_sched_group_barrier(0x200, kDsw, 0);                                   \
     }                                                                                         \
-    scale_add(cg, sv, (G) * KT + team < groups);                                              \
+    scale_add(cg, sv, kAllLive || (G) * KT + team < groups);                                  \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
     __syncthreads();                                                                          \
   }
@@ -366,6 +366,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     // the plain loop, whose last pass may run up to two bodies as no-ops:
     // the extra entry code would cost them their third wave per SIMD.
     constexpr bool kPeel = WM * WN > 4;
+    constexpr bool kAllLive = kPeel && KT == 1;  // every body has a group: no selects
     const int64_t rem = kPeel ? nloc % 3 : 0;
     if (rem == 0) {
       LOWBIT_GEMM_START1(s0, s1)
