@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   const int tid = (NT & (NT - 1)) == 0 ? (int)(threadIdx.x & (NT - 1))
                   : KT == 1             ? (int)threadIdx.x
                                         : (int)(threadIdx.x % NT);
-  const int team = KT == 1 ? 0 : (int)(threadIdx.x / NT);
+  const int team = KT == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x / NT));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -289,8 +289,10 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
       }
   };
   // acc += s * (sum of the chains); a group past the end leaves acc unchanged
+  // (`live` is wave-uniform: a scalar branch, not a select per accumulator)
   auto scale_add = [&](const f32x16 (&cg)[NCH][WBM][WBN], const float (&sv)[WBN], bool live)
       __attribute__((always_inline)) {
+    if (!live) return;
 #pragma unroll
     for (int bi = 0; bi < WBM; ++bi)
 #pragma unroll
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
         for (int v = 0; v < 16; ++v) {
           float f = __builtin_fmaf(sv[bj], cg[0][bi][bj][v], acc[bi][bj][v]);
           if constexpr (NCH == 2) f = __builtin_fmaf(sv[bj], cg[NCH - 1][bi][bj][v], f);
-          acc[bi][bj][v] = live ? f : acc[bi][bj][v];
+          acc[bi][bj][v] = f;
         }
   };
 
@@ -454,14 +456,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
       }                                                                                       \
     }                                                                                         \
     /* a group past the end (the last block of four) leaves acc unchanged */                 \
-    const bool live = (G) * KT + team < groups;                                               \
-    _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi)                                        \
-    _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj)                                        \
-    _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                          \
-      float f = __builtin_fmaf(sv[bj], cg[0][bi][bj][v], acc[bi][bj][v]);                     \
-      if constexpr (NCH == 2) f = __builtin_fmaf(sv[bj], cg[NCH - 1][bi][bj][v], f);          \
-      acc[bi][bj][v] = live ? f : acc[bi][bj][v];                                             \
-    }                                                                                         \
+    scale_add(cg, sv, (G) * KT + team < groups);                                              \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
     __syncthreads();                                                                          \
   }
