@@ -17,6 +17,14 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<1> { static constexpr int cell_bytes = 16; };
 template <> struct Fmt<2> { static constexpr int cell_bytes = 32; };
 
+// Raw buffer resource over [base, base + bytes) (bytes < 2^31): a load at an
+// offset past the end returns zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  constexpr int kRawBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferFlags);
+}
+
 // y[0 .. count) = 0 by the threads gid = 0, stride, 2 stride, ... of a grid:
 // 16-byte stores (y is 16-byte aligned), then the count % 4 tail.
 __device__ __forceinline__ void zero_f32(float* y, int64_t count, int64_t gid, int64_t stride) {

@@ -29,6 +29,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;
 constexpr int kThreads = 256;
@@ -138,31 +139,41 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   const int64_t chunks = k / kChunk;
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
 
+  // Loads go through buffer resources that cover this tile's rows of X, W
+  // codes and scales: the per-lane offsets are fixed, the group offset is a
+  // scalar, and an offset past a resource (rows of X past m, row tiles of W
+  // past the end) returns zeros.  Every resource stays below 2^31 bytes for
+  // k <= 2^22 (the library's limit).
+  const int64_t xrows = m - m0 < BM ? m - m0 : BM;
+  const int64_t wtiles0 = n0 / kTileRows;
+  const int64_t wtiles = ntiles - wtiles0 < BN / 16 ? ntiles - wtiles0 : BN / 16;
+  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(x + m0 * k, xrows * k * 2);
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(codes + wtiles0 * chunks * CB, wtiles * chunks * CB);
+  const __amdgpu_buffer_rsrc_t sres =
+      buffer_rsrc(scales + wtiles0 * groups * kTileRows, wtiles * groups * kTileRows * 2);
+
   // --- X staging: slot i = tid + NT*j is row i/16, 16-byte column i%16 of
-  // the group; rows past m read row m-1 (those outputs are never stored).
+  // the group (rows past m read zeros; those outputs are never stored).
   // When NT does not divide the slots, the last slot exists for the first
   // XS - NT*(XL-1) threads only (whole waves): the others load a valid row
   // and store nothing.
-  const uint16_t* xsrc[XL];
+  uint32_t xoff[XL];
   int xdst[XL];
   const bool xlast = !kXPartial || tid + NT * (XL - 1) < XS;
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int i = (j == XL - 1 && !xlast) ? tid : tid + NT * j;
-    int64_t row = m0 + (i >> 4);
-    if (row >= m) row = m - 1;
-    xsrc[j] = x + row * k + (i & 15) * 8;
+    xoff[j] = (uint32_t)((i >> 4) * k * 2 + (i & 15) * 16);
     xdst[j] = slot(i >> 4, i & 15);
   }
 
   // --- W codes: thread -> cell ci = tid % BN (row tile ci/16, chunk ci%16
   // of the group), rows part*RPT .. part*RPT + RPT-1 of that cell, part =
-  // tid / BN; eight consecutive lanes write one row, eight different slots
+  // tid / BN; eight consecutive lanes write one row, eight different slots.
+  // A tile past the end reads zero codes (Q1: -1, never stored; T2: 0).
   const int ci = tid % BN, part = tid / BN;
   const int wt = ci >> 4, wc = ci & 15;
-  const int64_t gtile = n0 / kTileRows + wt;
-  const bool wvalid = gtile < ntiles;
-  const uint8_t* wsrc = codes + ((wvalid ? gtile : 0) * chunks + wc) * CB + part * RPT;
+  const uint32_t woff = (uint32_t)((wt * chunks + wc) * CB + part * RPT);
   int wdst[RPT];
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) wdst[rr] = slot(wt * 16 + part * RPT + rr, wc);
@@ -171,18 +182,18 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   const int jl = lane & 31;
   int64_t ncol[WBN];
   bool nvalid[WBN];
-  const uint16_t* sptr[WBN];
+  uint32_t soff[WBN];
 #pragma unroll
   for (int bj = 0; bj < WBN; ++bj) {
     ncol[bj] = n0 + wn * (BN / WN) + bj * 32 + jl;
     nvalid[bj] = ncol[bj] < n;
-    const int64_t nn = nvalid[bj] ? ncol[bj] : 0;
-    sptr[bj] = scales + ((nn >> 4) * groups) * kTileRows + (nn & 15);
+    const int64_t nl = ncol[bj] - n0;
+    soff[bj] = (uint32_t)((((nl >> 4) * groups) * kTileRows + (nl & 15)) * 2);
   }
 
   // Prefetched data stays raw until it is used one iteration later (a
   // select on a just-loaded value would force an immediate wait).  Invalid
-  // tiles / columns load from valid addresses and are zeroed at use.
+  // columns are zeroed at use.
   constexpr int CW = (RPT * 1 + 3) / 4;  // code words per plane per thread
   struct Stage {
     u32x4 xr[XL];
@@ -190,27 +201,28 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     uint32_t sh[WBN];
   };
   auto fetch = [&](int64_t g, Stage& st) __attribute__((always_inline)) {
+    const int xg = (int)(g * BK * 2), wg = (int)(g * kChunksPerGroup * CB);
 #pragma unroll
-    for (int j = 0; j < XL; ++j) st.xr[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + g * BK);
-    const uint8_t* cell = wsrc + g * kChunksPerGroup * CB;
+    for (int j = 0; j < XL; ++j) st.xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j], xg, 0);
     if constexpr (RPT == 8) {
-      const uint2 a = *reinterpret_cast<const uint2*>(cell);
+      const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(wres, woff, wg, 0);
       st.p[0] = a.x;
       st.p[1] = a.y;
       if constexpr (FMT == 2) {
-        const uint2 c2 = *reinterpret_cast<const uint2*>(cell + 16);
+        const u32x2 c2 = __builtin_amdgcn_raw_buffer_load_b64(wres, woff + 16, wg, 0);
         st.q[0] = c2.x;
         st.q[1] = c2.y;
       }
     } else if constexpr (RPT == 2) {
-      st.p[0] = *reinterpret_cast<const uint16_t*>(cell);
-      if constexpr (FMT == 2) st.q[0] = *reinterpret_cast<const uint16_t*>(cell + 16);
+      st.p[0] = __builtin_amdgcn_raw_buffer_load_b16(wres, woff, wg, 0);
+      if constexpr (FMT == 2) st.q[0] = __builtin_amdgcn_raw_buffer_load_b16(wres, woff + 16, wg, 0);
     } else {
-      st.p[0] = *reinterpret_cast<const uint32_t*>(cell);
-      if constexpr (FMT == 2) st.q[0] = *reinterpret_cast<const uint32_t*>(cell + 16);
+      st.p[0] = __builtin_amdgcn_raw_buffer_load_b32(wres, woff, wg, 0);
+      if constexpr (FMT == 2) st.q[0] = __builtin_amdgcn_raw_buffer_load_b32(wres, woff + 16, wg, 0);
     }
 #pragma unroll
-    for (int bj = 0; bj < WBN; ++bj) st.sh[bj] = sptr[bj][g * kTileRows];
+    for (int bj = 0; bj < WBN; ++bj)
+      st.sh[bj] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[bj], (int)(g * kTileRows * 2), 0);
   };
   auto stash = [&](const Stage& st, int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -219,9 +231,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
         xs[team][b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
-      // codes of a tile past the end are replaced by zeros (Q1: -1, never
-      // stored; T2: 0)
-      const uint32_t pw = wvalid ? st.p[rr >> 2] : 0u;
+      const uint32_t pw = st.p[rr >> 2];
       uint32_t dp;
       switch (rr & 3) {
         case 0: dp = rep_byte<0>(pw); break;
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
       if constexpr (FMT == 1) {
         e = expand_q1(dp);
       } else {
-        const uint32_t qw = wvalid ? st.q[rr >> 2] : 0u;
+        const uint32_t qw = st.q[rr >> 2];
         uint32_t dq, dn;
         switch (rr & 3) {
           case 0: dq = rep_byte<0>(qw); dn = rep_byte<0>(pw ^ qw); break;
