@@ -120,7 +120,10 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tiles of 32 x 32 blocks");
 
   constexpr bool kSingle = kSingleBuffer<BM, BN, WM, WN>;
-  constexpr int NB = kSingle ? 1 : 2;  // LDS buffers per team
+  // tiles of more than four waves run one work-group per CU and have LDS to
+  // spare: their register ring stages into two LDS buffers
+  constexpr bool kWide = WM * WN > 4;
+  constexpr int NB = kSingle && !kWide ? 1 : 2;  // LDS buffers per team
   __shared__ uint4 xs[KT][NB][BM * kRowU4];
   __shared__ uint4 ws[KT][NB][BN * kRowU4];
 
@@ -316,47 +319,61 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   };
 
   if constexpr (kSingle) {
-    // Ring of three register stages over ONE LDS buffer: group g + 2 is
-    // fetched while group g is multiplied.  The operands of g are read from
-    // LDS in two halves of four k-steps; once every wave holds the second
-    // half (barrier), group g + 1 is written over them while the last four
-    // k-steps run.  Stages are separate variables and the body is written out
-    // three times, so no stage is indexed at run time.
+    // Ring of three register stages: group g + 2 is fetched while group g is
+    // multiplied.  The operands of g are read from LDS in two halves of four
+    // k-steps.  With ONE LDS buffer (2 x 2 waves, three work-groups per CU),
+    // once every wave holds the second half (barrier) group g + 1 is written
+    // over them while the last four k-steps run.  Wider tiles (one
+    // work-group per CU) alternate between two LDS buffers: group g + 1 goes
+    // to the other buffer with no mid-group barrier, for ternary codes spread
+    // over all eight k-steps.  Stages are separate variables and the body is
+    // written out three times, so no stage is indexed at run time.
     Stage s0, s1, s2;
     float sv[WBN];
     // staging VALU per MFMA of the second half (about 10 (Q1) / 21 (T2) per
     // expanded W row)
     constexpr int kValu = (RPT * (FMT == 1 ? 10 : 21) + 3) / 4;
     constexpr int kDsw = (XL + RPT + 3) / 4;  // staging LDS writes per MFMA
+    constexpr bool kSpread = kWide && FMT == 2;
+    constexpr int kValu8 = (kValu + 1) / 2, kDsw8 = (XL + RPT + 7) / 8;  // spread over 8
 #define LOWBIT_GEMM_ITER1(G, FAR, NEAR)                                                        \
   {                                                                                           \
+    const int RB = kWide ? (int)((G) & 1) : 0; /* LDS buffer of group G */                    \
     fetch(gof((G) + 2), FAR);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     f32x16 cg[NCH][WBM][WBN];                                                                 \
     bf16x8 a[4][WBM], bb[4][WBN];                                                             \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                           \
-      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = read_a(0, r, bi);         \
-      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = read_b(0, r, bj);        \
+      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = read_a(RB, r, bi);        \
+      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = read_b(RB, r, bj);       \
     }                                                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                        \
+    /* two buffers: group G + 1 is staged into the other one, across all */                   \
+    /* eight k-steps for ternary codes (1-bit ones would spill) */                            \
+    if constexpr (kSpread) stash(NEAR, RB ^ 1);                                               \
     /* steps 0..3, each followed by the reads of step r + 4 into its registers */            \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                           \
       mfma_step(cg, r, a[r], bb[r]);                                                          \
-      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = read_a(0, r + 4, bi);     \
-      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = read_b(0, r + 4, bj);    \
+      _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = read_a(RB, r + 4, bi);    \
+      _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = read_b(RB, r + 4, bj);   \
     }                                                                                         \
     _Pragma("unroll") for (int r = 0; r < 4 * WBM * WBN; ++r) {                               \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
       __builtin_amdgcn_sched_group_barrier(0x100, (WBM + WBN) / (WBM * WBN), 0);              \
+      if constexpr (kSpread) {                                                                \
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu8, 0);                               \
+        __builtin_amdgcn_sched_group_barrier(0x200, kDsw8, 0);                                \
+      }                                                                                       \
     }                                                                                         \
-    /* every wave holds its operands: the buffer may be overwritten */                       \
-    __syncthreads();                                                                          \
+    /* one buffer: once every wave holds its operands (barrier), group G + 1 */              \
+    /* is written over them during the last four k-steps */                                   \
+    if constexpr (!kWide) __syncthreads();                                                    \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) mfma_step(cg, r + 4, a[r], bb[r]);          \
-    stash(NEAR, 0);                                                                           \
+    if constexpr (!kSpread) stash(NEAR, RB ^ (int)kWide);                                     \
     _Pragma("unroll") for (int r = 0; r < 4 * WBM * WBN; ++r) {                               \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
-      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                                  \
-      __builtin_amdgcn_sched_group_barrier(0x200, kDsw, 0);                                   \
+      __builtin_amdgcn_sched_group_barrier(0x002, kSpread ? kValu8 : kValu, 0);               \
+      __builtin_amdgcn_sched_group_barrier(0x200, kSpread ? kDsw8 : kDsw, 0);                 \
     }                                                                                         \
     scale_add(cg, sv, kAllLive || (G) * KT + team < groups);                                  \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
