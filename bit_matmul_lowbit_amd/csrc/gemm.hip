@@ -39,21 +39,15 @@ constexpr int kRowU4 = BK / 8;  // 16-byte slots per LDS row
 __device__ __forceinline__ int slot(int r, int c) { return r * kRowU4 + (c ^ (r & 15)); }
 
 // Code byte -> 8 BF16 values, two per dword (k = 2p in the low half, 2p + 1
-// in the high half).  The byte is placed in the low byte of both 16-bit
+// in the high half).  Q1: the byte is placed in the low byte of both 16-bit
 // halves; a packed 16-bit shift by (15 - 2p, 14 - 2p) brings bits 2p and
 // 2p + 1 to bits 15 and 31, where v_bitop3 uses them as sign bits (+1 and
-// -1 differ only there); ternary also masks the pairs whose pos xor neg bit
-// is clear.  Two (Q1) or five (T2) VALU operations per dword.
+// -1 differ only there): two VALU operations per dword.  Ternary: below.
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pk_shl(uint32_t d, uint32_t sh) {
   const s16x2 a = __builtin_bit_cast(s16x2, d), s = __builtin_bit_cast(s16x2, sh);
   return __builtin_bit_cast(uint32_t, (s16x2)(a << s));
-}
-
-__device__ __forceinline__ uint32_t pk_mask15(uint32_t d) {
-  const s16x2 a = __builtin_bit_cast(s16x2, d);
-  return __builtin_bit_cast(uint32_t, (s16x2)(a >> (s16x2){15, 15}));
 }
 
 // byte J of w in the low byte of both halves
@@ -78,15 +72,36 @@ __device__ __forceinline__ uint4 expand_q1(uint32_t d) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// ternary: dn = pos xor neg, dq = neg  ->  +1, -1 or 0 (0 also when both set)
-__device__ __forceinline__ uint4 expand_t2(uint32_t dn, uint32_t dq) {
+// ternary: one row's pos xor neg byte in the low byte and its neg byte in
+// the high byte of both 16-bit halves.  A packed shift by (7 - k) puts
+// element k's nonzero bit at bit 7 and its neg bit at bit 15; bit 7 times
+// 0x7F is exactly 0x3F80 (BF16 1.0), and v_bitop3 ORs in the sign: +1, -1
+// or 0 (-0 when both bits are set).  Four VALU operations per dword.
+__device__ __forceinline__ uint32_t pk_mul_lo(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) * __builtin_bit_cast(u16x2, b));
+}
+
+template <int P>
+constexpr uint32_t kTritShift = ((uint32_t)(6 - 2 * P) << 16) | (uint32_t)(7 - 2 * P);
+
+__device__ __forceinline__ uint4 expand_t2(uint32_t comb) {
   uint32_t v[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const uint32_t sh = p == 0 ? kPairShift<0> : p == 1 ? kPairShift<1> : p == 2 ? kPairShift<2> : kPairShift<3>;
-    v[p] = (kOnes | (pk_shl(dq, sh) & kSignBits)) & pk_mask15(pk_shl(dn, sh));
+    const uint32_t sh = p == 0 ? kTritShift<0> : p == 1 ? kTritShift<1> : p == 2 ? kTritShift<2> : kTritShift<3>;
+    const uint32_t h = pk_shl(comb, sh);
+    v[p] = (h & kSignBits) | pk_mul_lo(h & 0x00800080u, 0x007F007Fu);
   }
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// the byte-J pair of a ternary row: pos xor neg (low byte of each half), neg
+// (high byte)
+template <int J>
+__device__ __forceinline__ uint32_t trit_pair(uint32_t pw, uint32_t qw) {
+  return __builtin_amdgcn_perm(qw, pw ^ qw, (uint32_t)J | ((uint32_t)(4 + J) << 8) |
+                                                ((uint32_t)J << 16) | ((uint32_t)(4 + J) << 24));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -235,27 +250,26 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const uint32_t pw = st.p[rr >> 2];
-      uint32_t dp;
-      switch (rr & 3) {
-        case 0: dp = rep_byte<0>(pw); break;
-        case 1: dp = rep_byte<1>(pw); break;
-        case 2: dp = rep_byte<2>(pw); break;
-        default: dp = rep_byte<3>(pw); break;
-      }
       uint4 e;
       if constexpr (FMT == 1) {
+        uint32_t dp;
+        switch (rr & 3) {
+          case 0: dp = rep_byte<0>(pw); break;
+          case 1: dp = rep_byte<1>(pw); break;
+          case 2: dp = rep_byte<2>(pw); break;
+          default: dp = rep_byte<3>(pw); break;
+        }
         e = expand_q1(dp);
       } else {
         const uint32_t qw = st.q[rr >> 2];
-        uint32_t dq, dn;
+        uint32_t comb;
         switch (rr & 3) {
-          case 0: dq = rep_byte<0>(qw); dn = rep_byte<0>(pw ^ qw); break;
-          case 1: dq = rep_byte<1>(qw); dn = rep_byte<1>(pw ^ qw); break;
-          case 2: dq = rep_byte<2>(qw); dn = rep_byte<2>(pw ^ qw); break;
-          default: dq = rep_byte<3>(qw); dn = rep_byte<3>(pw ^ qw); break;
+          case 0: comb = trit_pair<0>(pw, qw); break;
+          case 1: comb = trit_pair<1>(pw, qw); break;
+          case 2: comb = trit_pair<2>(pw, qw); break;
+          default: comb = trit_pair<3>(pw, qw); break;
         }
-        (void)dp;
-        e = expand_t2(dn, dq);
+        e = expand_t2(comb);
       }
       ws[team][b][wdst[rr]] = e;
     }
@@ -319,26 +333,29 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   };
 
   if constexpr (kSingle) {
-    // Ring of three register stages: group g + 2 is fetched while group g is
-    // multiplied.  The operands of g are read from LDS in two halves of four
-    // k-steps.  With ONE LDS buffer (2 x 2 waves, three work-groups per CU),
-    // once every wave holds the second half (barrier) group g + 1 is written
-    // over them while the last four k-steps run.  Wider tiles (one
-    // work-group per CU) alternate between two LDS buffers: group g + 1 goes
-    // to the other buffer with no mid-group barrier, for ternary codes spread
-    // over all eight k-steps.  Stages are separate variables and the body is
-    // written out three times, so no stage is indexed at run time.
-    Stage s0, s1, s2;
+    // Two register stages: group g + 2 is fetched (into the stage group g
+    // was staged from, one body earlier) while group g is multiplied and
+    // group g + 1 is staged into LDS.  The operands of g are read from LDS in
+    // two halves of four k-steps.  With ONE LDS buffer (2 x 2 waves, three
+    // work-groups per CU), once every wave holds the second half (barrier)
+    // group g + 1 is written over them while the last four k-steps run.
+    // Wider tiles (one work-group per CU) alternate between two LDS buffers:
+    // group g + 1 goes to the other buffer with no mid-group barrier, for
+    // ternary codes spread over all eight k-steps.  Stages are separate
+    // variables and the body is written out twice, so neither a stage nor a
+    // buffer is indexed at run time (buffer offsets fold into the LDS
+    // instructions' immediate offsets).
+    Stage s0, s1;
     float sv[WBN];
-    // staging VALU per MFMA of the second half (about 10 (Q1) / 21 (T2) per
+    // staging VALU per MFMA of the second half (about 10 (Q1) / 17 (T2) per
     // expanded W row)
-    constexpr int kValu = (RPT * (FMT == 1 ? 10 : 21) + 3) / 4;
+    constexpr int kValu = (RPT * (FMT == 1 ? 10 : 17) + 3) / 4;
     constexpr int kDsw = (XL + RPT + 3) / 4;  // staging LDS writes per MFMA
     constexpr bool kSpread = kWide && FMT == 2;
     constexpr int kValu8 = (kValu + 1) / 2, kDsw8 = (XL + RPT + 7) / 8;  // spread over 8
-#define LOWBIT_GEMM_ITER1(G, FAR, NEAR)                                                        \
+#define LOWBIT_GEMM_ITER1(G, FAR, NEAR, BUF)                                                   \
   {                                                                                           \
-    const int RB = kWide ? (int)((G) & 1) : 0; /* LDS buffer of group G */                    \
+    constexpr int RB = kWide ? (BUF) : 0; /* LDS buffer of group G */                         \
     fetch(gof((G) + 2), FAR);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     f32x16 cg[NCH][WBM][WBN];                                                                 \
@@ -379,40 +396,35 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(NEAR, bj);           \
     __syncthreads();                                                                          \
   }
-#define LOWBIT_GEMM_START1(FIRST, SECOND)                                                      \
+#define LOWBIT_GEMM_START1(FIRST, SECOND, BUF)                                                 \
   {                                                                                           \
     fetch(gof(0), FIRST);                                                                     \
     fetch(gof(1), SECOND);                                                                    \
-    stash(FIRST, 0);                                                                          \
+    stash(FIRST, kWide ? (BUF) : 0);                                                          \
     _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) sv[bj] = scale_of(FIRST, bj);          \
     __syncthreads();                                                                          \
   }
-    // The loop body is entered with group g in LDS and group g + 1 in s1.
-    // When the group count is not a multiple of three, the first one or two
-    // groups run before the loop with the stages named so that they leave
-    // exactly that state: no group body runs past the end (a group past the
-    // end of one K-team still runs as a no-op).  The 2 x 2 wave kernels keep
-    // the plain loop, whose last pass may run up to two bodies as no-ops:
-    // the extra entry code would cost them their third wave per SIMD.
+    // The loop body is entered with group g in LDS buffer 0, group g + 1 in
+    // s1 and s0 free.  With an odd group count the first group runs before
+    // the loop, with the stages and buffers named so that it leaves exactly
+    // that state: no group body runs past the end (a group past the end of
+    // one K-team still runs as a no-op).  The 2 x 2 wave kernels keep the
+    // plain loop, whose last pass may run one body as a no-op: the extra
+    // entry code would cost them their third wave per SIMD.
     constexpr bool kPeel = WM * WN > 4;
     constexpr bool kAllLive = kPeel && KT == 1;  // every body has a group: no selects
-    const int64_t rem = kPeel ? nloc % 3 : 0;
+    const int64_t rem = kPeel ? nloc % 2 : 0;
     if (rem == 0) {
-      LOWBIT_GEMM_START1(s0, s1)
-    } else if (rem == 1) {
-      LOWBIT_GEMM_START1(s2, s0)
-      LOWBIT_GEMM_ITER1(0, s1, s0)
+      LOWBIT_GEMM_START1(s0, s1, 0)
     } else {
-      LOWBIT_GEMM_START1(s1, s2)
-      LOWBIT_GEMM_ITER1(0, s0, s2)
-      LOWBIT_GEMM_ITER1(1, s1, s0)
+      LOWBIT_GEMM_START1(s1, s0, 1)
+      LOWBIT_GEMM_ITER1(0, s1, s0, 1)
     }
     // Branch-free body (a branch would let the compiler sink the prefetch
     // loads into the blocks that consume them).
-    for (int64_t g = rem; g < nloc; g += 3) {
-      LOWBIT_GEMM_ITER1(g, s2, s1)
-      LOWBIT_GEMM_ITER1(g + 1, s0, s2)
-      LOWBIT_GEMM_ITER1(g + 2, s1, s0)
+    for (int64_t g = rem; g < nloc; g += 2) {
+      LOWBIT_GEMM_ITER1(g, s0, s1, 0)
+      LOWBIT_GEMM_ITER1(g + 1, s1, s0, 1)
     }
 #undef LOWBIT_GEMM_START1
 #undef LOWBIT_GEMM_ITER1
