@@ -135,9 +135,10 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tiles of 32 x 32 blocks");
 
   constexpr bool kSingle = kSingleBuffer<BM, BN, WM, WN>;
-  // tiles of more than four waves run one work-group per CU and have LDS to
-  // spare: their register ring stages into two LDS buffers
-  constexpr bool kWide = WM * WN > 4;
+  // work-groups of more than four waves (wide tiles, or two K-teams) run
+  // alone on a CU and have LDS to spare: their register ring stages into two
+  // LDS buffers per team
+  constexpr bool kWide = WM * WN > 4 || KT > 1;
   constexpr int NB = kSingle && !kWide ? 1 : 2;  // LDS buffers per team
   __shared__ uint4 xs[KT][NB][BM * kRowU4];
   __shared__ uint4 ws[KT][NB][BN * kRowU4];
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     // two halves of four k-steps.  With ONE LDS buffer (2 x 2 waves, three
     // work-groups per CU), once every wave holds the second half (barrier)
     // group g + 1 is written over them while the last four k-steps run.
-    // Wider tiles (one work-group per CU) alternate between two LDS buffers:
+    // Work-groups alone on a CU alternate between two LDS buffers:
     // group g + 1 goes to the other buffer with no mid-group barrier, for
     // ternary codes spread over all eight k-steps.  Stages are separate
     // variables and the body is written out twice, so neither a stage nor a
