@@ -276,10 +276,9 @@ __device__ __forceinline__ void tile_lookups(const TileRegs<FMT>& tr, const char
 
 // Reduction of a tile's 16 row partials: within the group, scale the two
 // rows each lane is left with (scale word `sw`, zero for inactive lanes),
-// across the groups, then one atomic add per row (skipped for tiles past the
-// end: `live` is wave-uniform).  T2 halves its sums here.
+// across the groups, then one atomic add per row.  T2 halves its sums here.
 template <int FMT, int CH>
-__device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, bool live, int lane,
+__device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, int lane,
                                            int col, int b, int64_t t, int64_t n,
                                            float* __restrict__ y) {
   int row_off;
@@ -292,7 +291,7 @@ __device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, bool l
 #pragma unroll
   for (int j = 0; j < nv; ++j) {
     const int64_t row = t * kTileRows + row_off + j;
-    if (live && writer && col < b && row < n) atomicAdd(y + (int64_t)col * n + row, acc[j]);
+    if (writer && col < b && row < n) atomicAdd(y + (int64_t)col * n + row, acc[j]);
   }
 }
 
@@ -422,18 +421,28 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
   tile_lookups<FMT>(buf[0], tbase, lane_base, acc0);
   uint32_t sw_cur = active ? buf[0].sc : 0u;
   constexpr int U = (D % 2 == 0) ? D : 2 * D;  // multiple of the ring and of 2
-  while (t < tb) {
+  // step i of a pass (i is a constant once the loops below are unrolled)
+  auto step = [&](int i) __attribute__((always_inline)) {
+    float (&cur)[16] = (i & 1) ? acc1 : acc0;
+    float (&nxt)[16] = (i & 1) ? acc0 : acc1;
+    load_next(buf[(i + D - 1) % D]);
+    tile_lookups<FMT>(buf[(i + 1) % D], tbase, lane_base, nxt);
+    const uint32_t sw_nxt = active ? buf[(i + 1) % D].sc : 0u;
+    tile_store<FMT, CH>(cur, sw_cur, lane, col, b, t, n, y);
+    sw_cur = sw_nxt;
+    t += stride;
+  };
+  // whole passes while all U tiles of the pass exist, then the last tiles one
+  // by one (a wave of a small matrix may have a single tile: the rest of a
+  // pass would be spent on lookups and reductions of empty tiles)
+  while (t + (U - 1) * stride < tb) {
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      float (&cur)[16] = (i & 1) ? acc1 : acc0;
-      float (&nxt)[16] = (i & 1) ? acc0 : acc1;
-      load_next(buf[(i + D - 1) % D]);
-      tile_lookups<FMT>(buf[(i + 1) % D], tbase, lane_base, nxt);
-      const uint32_t sw_nxt = active ? buf[(i + 1) % D].sc : 0u;
-      tile_store<FMT, CH>(cur, sw_cur, t < tb, lane, col, b, t, n, y);
-      sw_cur = sw_nxt;
-      t += stride;
-    }
+    for (int i = 0; i < U; ++i) step(i);
+  }
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    if (t >= tb) break;
+    step(i);
   }
 }
 
