@@ -140,7 +140,10 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   // LDS buffers per team
   constexpr bool kWide = WM * WN > 4 || KT > 1;
   constexpr int NB = kSingle && !kWide ? 1 : 2;  // LDS buffers per team
-  __shared__ uint4 xs[KT][NB][BM * kRowU4];
+  // X buffers are separate arrays so that loads straight into one of them
+  // are not taken to alias reads of the other
+  __shared__ uint4 xs0[KT][BM * kRowU4];
+  __shared__ uint4 xs1[KT][NB > 1 ? BM * kRowU4 : 1];
   __shared__ uint4 ws[KT][NB][BN * kRowU4];
 
   // KT teams of NT threads share the output tile; team t takes the groups
@@ -151,6 +154,9 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   const int team = KT == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x / NT));
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  auto xbuf = [&](int b) __attribute__((always_inline)) -> uint4* {
+    return b == 0 ? &xs0[team][0] : &xs1[team][0];
+  };
   const int wm = wave / WN, wn = wave % WN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
@@ -185,6 +191,37 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     xoff[j] = (uint32_t)((i >> 4) * k * 2 + (i & 15) * 16);
     xdst[j] = slot(i >> 4, i & 15);
   }
+
+  // --- X straight into LDS (two-buffer kernels): DMA round j of wave w
+  // fills slots w * 64 + j * NT .. + 63 (lane l the slot + l); slot p holds
+  // row p / 16 and 16-byte column (p % 16) ^ (row % 16), the swizzle above.
+  // The last round exists for the waves whose slots are below XS.  (The
+  // two-team kernel measured slower this way and keeps the register path.)
+  constexpr bool kDma = kWide && KT == 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t xdma[XL];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int p = wv * 64 + j * NT + lane;
+    const int r = p >> 4, c = (p & 15) ^ (r & 15);
+    xdma[j] = (uint32_t)(r * k * 2 + c * 16);
+  }
+  auto dma_x = [&](int64_t g, int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int p0 = wv * 64 + j * NT;
+      // (device pass only: the host pass has no LDS address space for the
+      // builtin's operand, and would drop the kernel's launch stub)
+#if defined(__HIP_DEVICE_COMPILE__)
+      if (j < XL - 1 || p0 < XS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, (__attribute__((address_space(3))) void*)(xbuf(b) + p0), 16, xdma[j],
+            (int)(g * BK * 2), 0, 0);
+#else
+      (void)p0;
+#endif
+    }
+  };
 
   // --- W codes: thread -> cell ci = tid % BN (row tile ci/16, chunk ci%16
   // of the group), rows part*RPT .. part*RPT + RPT-1 of that cell, part =
@@ -221,8 +258,10 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   };
   auto fetch = [&](int64_t g, Stage& st) __attribute__((always_inline)) {
     const int xg = (int)(g * BK * 2), wg = (int)(g * kChunksPerGroup * CB);
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j) st.xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j], xg, 0);
+      for (int j = 0; j < XL; ++j) st.xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j], xg, 0);
+    }
     if constexpr (RPT == 8) {
       const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(wres, woff, wg, 0);
       st.p[0] = a.x;
@@ -244,10 +283,12 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
       st.sh[bj] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[bj], (int)(g * kTileRows * 2), 0);
   };
   auto stash = [&](const Stage& st, int b) __attribute__((always_inline)) {
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int j = 0; j < XL; ++j)
-      if (j < XL - 1 || xlast)
-        xs[team][b][xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
+      for (int j = 0; j < XL; ++j)
+        if (j < XL - 1 || xlast)
+          xbuf(b)[xdst[j]] = make_uint4(st.xr[j].x, st.xr[j].y, st.xr[j].z, st.xr[j].w);
+    }
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const uint32_t pw = st.p[rr >> 2];
@@ -299,7 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   // (even and odd k-steps), so consecutive MFMAs do not wait on each other
   constexpr int NCH = (WBM * WBN == 1 && !kSingle) ? 2 : 1;
   auto read_a = [&](int b, int step, int bi) __attribute__((always_inline)) {
-    return __builtin_bit_cast(bf16x8, xs[team][b][slot(wm * (BM / WM) + bi * 32 + jl, step * 2 + kh)]);
+    return __builtin_bit_cast(bf16x8, xbuf(b)[slot(wm * (BM / WM) + bi * 32 + jl, step * 2 + kh)]);
   };
   auto read_b = [&](int b, int step, int bj) __attribute__((always_inline)) {
     return __builtin_bit_cast(bf16x8, ws[team][b][slot(wn * (BN / WN) + bj * 32 + jl, step * 2 + kh)]);
@@ -357,6 +398,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
 #define LOWBIT_GEMM_ITER1(G, FAR, NEAR, BUF)                                                   \
   {                                                                                           \
     constexpr int RB = kWide ? (BUF) : 0; /* LDS buffer of group G */                         \
+    if constexpr (kDma) dma_x(gof((G) + 1), RB ^ 1);                                          \
     fetch(gof((G) + 2), FAR);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     f32x16 cg[NCH][WBM][WBN];                                                                 \
@@ -399,6 +441,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   }
 #define LOWBIT_GEMM_START1(FIRST, SECOND, BUF)                                                 \
   {                                                                                           \
+    if constexpr (kDma) dma_x(gof(0), BUF);                                                   \
     fetch(gof(0), FIRST);                                                                     \
     fetch(gof(1), SECOND);                                                                    \
     stash(FIRST, kWide ? (BUF) : 0);                                                          \
@@ -464,7 +507,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
       bf16x8 a[RS][WBM], bb[RS][WBN];                                                         \
       _Pragma("unroll") for (int r = 0; r < RS; ++r) {                                        \
         _Pragma("unroll") for (int bi = 0; bi < WBM; ++bi) a[r][bi] = __builtin_bit_cast(     \
-            bf16x8, xs[team][B][slot(wm * (BM / WM) + bi * 32 + jl, (s0 + r) * 2 + kh)]);           \
+            bf16x8, xbuf(B)[slot(wm * (BM / WM) + bi * 32 + jl, (s0 + r) * 2 + kh)]);              \
         _Pragma("unroll") for (int bj = 0; bj < WBN; ++bj) bb[r][bj] = __builtin_bit_cast(    \
             bf16x8, ws[team][B][slot(wn * (BN / WN) + bj * 32 + jl, (s0 + r) * 2 + kh)]);           \
       }                                                                                       \
@@ -516,7 +559,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     // teams 1.. leave their sums in their own (no longer read) LDS buffers;
     // team 0 adds them and stores the tile
     if (team > 0) {
-      float* red = reinterpret_cast<float*>(&xs[team][0][0]);
+      float* red = reinterpret_cast<float*>(&xs0[team][0]);
 #pragma unroll
       for (int bi = 0; bi < WBM; ++bi)
 #pragma unroll
@@ -528,7 +571,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     if (team > 0) return;
 #pragma unroll
     for (int t = 1; t < KT; ++t) {
-      const float* red = reinterpret_cast<const float*>(&xs[t][0][0]);
+      const float* red = reinterpret_cast<const float*>(&xs0[t][0]);
 #pragma unroll
       for (int bi = 0; bi < WBM; ++bi)
 #pragma unroll
