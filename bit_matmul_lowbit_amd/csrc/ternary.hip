@@ -36,9 +36,12 @@ __device__ __forceinline__ bool twice_gt(uint32_t m, uint32_t S) {
   return d > S;
 }
 
-// One lane per 8-weight chunk c of one 16-row tile, as the 1-bit quantiser:
-// load 16 rows x 8 weights, reduce the group maxima over the 16 lanes of a
-// group, then decide every weight against its row's maximum.
+// One lane per 8-weight chunk c of one 16-row tile, as the 1-bit quantiser.
+// A (rolled) loop over four blocks of four rows: load them, reduce their
+// group maxima over the 16 lanes of the group (two 16-bit maxima per
+// shuffle), decide their 32 weights, and shift the block's pos and neg code
+// words into place.  Only one block is live at a time, so the kernel keeps
+// enough waves in flight to stream at HBM speed.
 __global__ __launch_bounds__(kBlock) void quantize_t2_kernel(const uint16_t* __restrict__ w,
                                                              int64_t n, int64_t k,
                                                              uint8_t* __restrict__ codes,
@@ -47,53 +50,61 @@ __global__ __launch_bounds__(kBlock) void quantize_t2_kernel(const uint16_t* __r
   const int64_t tile = blockIdx.x;
   const int64_t c = (int64_t)blockIdx.y * kBlock + threadIdx.x;
   if (c >= chunks) return;  // whole 16-lane groups leave together
-  uint32_t hw[kTileRows][4];
-  uint32_t mags[8];
+  const int jr = (int)(c % kChunksPerGroup);  // this lane writes the scale of row jr
+  uint32_t p0 = 0u, p1 = 0u, p2 = 0u, p3 = 0u, q0 = 0u, q1 = 0u, q2 = 0u, q3 = 0u;
+  uint32_t my_scale = 0u;
+#pragma unroll 1
+  for (int blk = 0; blk < kTileRows / 4; ++blk) {
+    uint32_t hw[4][4];
 #pragma unroll
-  for (int r = 0; r < kTileRows; ++r) {
-    const int64_t row = tile * kTileRows + r;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < n) v = *reinterpret_cast<const uint4*>(w + row * k + c * kChunk);
-    hw[r][0] = v.x; hw[r][1] = v.y; hw[r][2] = v.z; hw[r][3] = v.w;
-    uint32_t mx = 0u;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) mx = max(mx, (hw[r][j >> 1] >> ((j & 1) * 16)) & 0x7FFFu);
-    if (r & 1) mags[r >> 1] |= mx << 16;
-    else mags[r >> 1] = mx;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int d = 8; d >= 1; d >>= 1)
-      mags[i] = max_u16x2(mags[i], (uint32_t)__shfl_xor((int)mags[i], d, 16));
-  }
-  uint32_t pos[4] = {0u, 0u, 0u, 0u}, neg[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int r = 0; r < kTileRows; ++r) {
-    const uint32_t S = (r & 1) ? (mags[r >> 1] >> 16) : (mags[r >> 1] & 0xFFFFu);
-    uint32_t pb = 0u, nb = 0u;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const uint32_t h = (hw[r][j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-      const uint32_t nz = twice_gt(h & 0x7FFFu, S) ? 1u : 0u;
-      const uint32_t sgn = h >> 15;
-      pb |= (nz & (sgn ^ 1u)) << j;
-      nb |= (nz & sgn) << j;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = tile * kTileRows + 4 * blk + u;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < n) v = *reinterpret_cast<const uint4*>(w + row * k + c * kChunk);
+      hw[u][0] = v.x; hw[u][1] = v.y; hw[u][2] = v.z; hw[u][3] = v.w;
     }
-    pos[r >> 2] |= pb << ((r & 3) * 8);
-    neg[r >> 2] |= nb << ((r & 3) * 8);
+    uint32_t pw = 0u, nw = 0u;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      // max |w| patterns of rows 2 pr (low half) and 2 pr + 1 of the block
+      uint32_t mags = 0u;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j)
+          mx = max(mx, (hw[2 * pr + u][j >> 1] >> ((j & 1) * 16)) & 0x7FFFu);
+        mags |= mx << (16 * u);
+      }
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1)
+        mags = max_u16x2(mags, (uint32_t)__shfl_xor((int)mags, d, 16));
+      if ((jr >> 1) == 2 * blk + pr) my_scale = (jr & 1) ? (mags >> 16) : (mags & 0xFFFFu);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t S = (mags >> (16 * u)) & 0xFFFFu;
+        uint32_t pb = 0u, nb = 0u;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const uint32_t h = (hw[2 * pr + u][j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+          const uint32_t nz = twice_gt(h & 0x7FFFu, S) ? 1u : 0u;
+          const uint32_t sgn = h >> 15;
+          pb |= (nz & (sgn ^ 1u)) << j;
+          nb |= (nz & sgn) << j;
+        }
+        pw |= pb << ((2 * pr + u) * 8);
+        nw |= nb << ((2 * pr + u) * 8);
+      }
+    }
+    // rows 4 blk .. 4 blk + 3 are code word blk: shift the words into place
+    p0 = p1; p1 = p2; p2 = p3; p3 = pw;
+    q0 = q1; q1 = q2; q2 = q3; q3 = nw;
   }
   uint8_t* cell = codes + (tile * chunks + c) * 32;
-  *reinterpret_cast<uint4*>(cell) = make_uint4(pos[0], pos[1], pos[2], pos[3]);
-  *reinterpret_cast<uint4*>(cell + 16) = make_uint4(neg[0], neg[1], neg[2], neg[3]);
-  const int jr = (int)(c % kChunksPerGroup);  // this lane writes the scale of row jr
-  uint32_t sel = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i == (jr >> 1)) sel = mags[i];
+  *reinterpret_cast<uint4*>(cell) = make_uint4(p0, p1, p2, p3);
+  *reinterpret_cast<uint4*>(cell + 16) = make_uint4(q0, q1, q2, q3);
   const int64_t groups = k / kGroup;
-  scales[(tile * groups + c / kChunksPerGroup) * kTileRows + jr] =
-      (uint16_t)((jr & 1) ? (sel >> 16) : (sel & 0xFFFFu));
+  scales[(tile * groups + c / kChunksPerGroup) * kTileRows + jr] = (uint16_t)my_scale;
 }
 
 // t of (row, col) from the two planes: pos - neg
