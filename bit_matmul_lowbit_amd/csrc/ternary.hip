@@ -107,86 +107,137 @@ __global__ __launch_bounds__(kBlock) void quantize_t2_kernel(const uint16_t* __r
   scales[(tile * groups + c / kChunksPerGroup) * kTileRows + jr] = (uint16_t)my_scale;
 }
 
-// t of (row, col) from the two planes: pos - neg
-__device__ __forceinline__ int trit(const uint8_t* __restrict__ codes, int64_t chunks, int64_t row,
-                                    int64_t col) {
-  const uint8_t* cell = codes + ((row / kTileRows) * chunks + col / kChunk) * 32;
-  const int r = (int)(row % kTileRows), b = (int)(col % kChunk);
-  return (int)((cell[r] >> b) & 1u) - (int)((cell[16 + r] >> b) & 1u);
-}
+// Base-3 conversions: one work-group per 16-row tile, over K-blocks of 1280
+// weights (256 base-3 bytes per row; a multiple of 5, 8 and 128, so no byte
+// straddles two blocks) staged in LDS, so that HBM sees whole code cells
+// and whole row segments.
+constexpr int kKB = 1280;
+constexpr int kKBChunks = kKB / kChunk;  // 160 code cells per tile and block
+constexpr int kKBBytes = kKB / 5;        // 256 base-3 bytes per row and block
 
-// two-plane codes + tile-major scales -> base-3 bytes + row-major scales;
-// one thread per output byte (then per output scale), grid-stride
+// two-plane codes + tile-major scales -> base-3 bytes + row-major scales.
+// Thread t writes bytes 16 (t % 16) .. + 15 of the block of row t / 16: their
+// 80 weights are chunks 10 (t % 16) .. + 9, whose pos and neg bytes it reads
+// from LDS; a 1024-entry table maps (pos bits, neg bits) of 5 weights to the
+// byte.
 __global__ __launch_bounds__(kBlock) void t2_to_base3_kernel(const uint8_t* __restrict__ codes,
                                                              const uint16_t* __restrict__ scales,
                                                              int64_t n, int64_t k,
                                                              uint8_t* __restrict__ out,
                                                              uint16_t* __restrict__ out_scales) {
+  __shared__ uint4 cells[kKBChunks * 2];
+  __shared__ uint8_t byte_of[1024];
+  const int64_t tile = blockIdx.x;
   const int64_t chunks = k / kChunk, groups = k / kGroup, rb = (k + 4) / 5;
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  for (int64_t i = gid; i < n * rb; i += stride) {
-    const int64_t row = i / rb, j = i - row * rb;
-    int v = 0, p = 1;
-#pragma unroll
+  const int t = threadIdx.x;
+  for (int e = t; e < 1024; e += kBlock) {
+    const int pb = e >> 5, nb = e & 31;
+    int v = 0, pw = 1;
     for (int q = 0; q < 5; ++q) {
-      const int64_t col = 5 * j + q;
-      v += ((col < k ? trit(codes, chunks, row, col) : 0) + 1) * p;
-      p *= 3;
+      v += (((pb >> q) & 1) - ((nb >> q) & 1) + 1) * pw;
+      pw *= 3;
     }
-    out[i] = (uint8_t)v;
+    byte_of[e] = (uint8_t)v;
   }
-  for (int64_t i = gid; i < n * groups; i += stride) {
-    const int64_t row = i / groups, g = i - row * groups;
-    out_scales[i] = scales[((row / kTileRows) * groups + g) * kTileRows + row % kTileRows];
+  const int r = t >> 4, bg = t & 15;
+  const int64_t row = tile * kTileRows + r;
+  const uint8_t* cb = reinterpret_cast<const uint8_t*>(cells);
+  for (int64_t k0 = 0; k0 < k; k0 += kKB) {
+    const int64_t c0 = k0 / kChunk;
+    const int nc = (int)(chunks - c0 < kKBChunks ? chunks - c0 : kKBChunks);
+    __syncthreads();  // the previous block's cells have been read
+    for (int i = t; i < kKBChunks * 2; i += kBlock)
+      cells[i] = i < nc * 2 ? reinterpret_cast<const uint4*>(codes + (tile * chunks + c0) * 32)[i]
+                            : make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    if (row >= n) continue;
+    // the 80 pos / neg bits of this thread's weights, in two 40-bit halves
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint64_t P = 0, N = 0;
+#pragma unroll
+      for (int cc = 0; cc < 5; ++cc) {
+        const int c = bg * 10 + h * 5 + cc;
+        P |= (uint64_t)cb[c * 32 + r] << (8 * cc);
+        N |= (uint64_t)cb[c * 32 + 16 + r] << (8 * cc);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int64_t jo = k0 / 5 + bg * 16 + h * 8 + jj;  // byte of the row
+        if (jo < rb)
+          out[row * rb + jo] = byte_of[(((P >> (5 * jj)) & 31) << 5) | ((N >> (5 * jj)) & 31)];
+      }
+    }
+  }
+  for (int i = t; i < kTileRows * groups; i += kBlock) {
+    const int rr = (int)(i / groups);
+    const int64_t g = i - (int64_t)rr * groups, rw = tile * kTileRows + rr;
+    if (rw < n) out_scales[rw * groups + g] = scales[(tile * groups + g) * kTileRows + rr];
   }
 }
 
-// base-3 bytes + row-major scales -> two-plane codes + tile-major scales;
-// one lane per (tile, chunk) as the ternary packer (rows past n get zero
-// codes and zero scales); a byte of 243..255 decodes with its fifth digit
-// taken mod 3
+// base-3 bytes + row-major scales -> two-plane codes + tile-major scales.  The
+// block's 16 row segments are staged in LDS (rows past n as byte 121: every
+// digit 1, t = 0).  An item (chunk, row) takes the two or three bytes that
+// hold its 8 weights, looks up their digits (a table of the five digits of
+// every byte value; a byte of 243..255 decodes with its fifth digit taken
+// mod 3) and writes its pos and neg bytes into the block's cells in LDS,
+// which then go out as whole 16-byte vectors.
 __global__ __launch_bounds__(kBlock) void base3_to_t2_kernel(const uint8_t* __restrict__ in,
                                                              const uint16_t* __restrict__ in_scales,
                                                              int64_t n, int64_t k,
                                                              uint8_t* __restrict__ codes,
                                                              uint16_t* __restrict__ scales) {
-  const int64_t chunks = k / kChunk, groups = k / kGroup, rb = (k + 4) / 5;
+  __shared__ uint8_t seg[kTileRows][kKBBytes];
+  __shared__ uint4 cells[kKBChunks * 2];
+  __shared__ uint16_t digits[256];  // digit q (= t + 1) in bits 2q, 2q + 1
   const int64_t tile = blockIdx.x;
-  const int64_t c = (int64_t)blockIdx.y * kBlock + threadIdx.x;
-  if (c >= chunks) return;
-  uint32_t pos[4] = {0u, 0u, 0u, 0u}, neg[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int r = 0; r < kTileRows; ++r) {
-    const int64_t row = tile * kTileRows + r;
-    uint32_t pb = 0u, nb = 0u;
-    if (row < n) {
-      const uint8_t* src = in + row * rb;
+  const int64_t chunks = k / kChunk, groups = k / kGroup, rb = (k + 4) / 5;
+  const int t = threadIdx.x;
+  {
+    int d = t, code = 0;
+    for (int q = 0; q < 5; ++q) {
+      code |= (d % 3) << (2 * q);
+      d /= 3;
+    }
+    digits[t] = (uint16_t)code;
+  }
+  uint8_t* cb = reinterpret_cast<uint8_t*>(cells);
+  for (int64_t k0 = 0; k0 < k; k0 += kKB) {
+    const int64_t c0 = k0 / kChunk;
+    const int nc = (int)(chunks - c0 < kKBChunks ? chunks - c0 : kKBChunks);
+    __syncthreads();  // the previous block's segments and cells have been read
+    for (int i = t; i < kTileRows * kKBBytes; i += kBlock) {
+      const int rr = i / kKBBytes, jb = i % kKBBytes;
+      const int64_t rw = tile * kTileRows + rr, jo = k0 / 5 + jb;
+      seg[rr][jb] = (rw < n && jo < rb) ? in[rw * rb + jo] : (uint8_t)121;
+    }
+    __syncthreads();
+    for (int it = t; it < nc * kTileRows; it += kBlock) {
+      const int c = it >> 4, rr = it & 15;
+      const int j0 = (c * kChunk) / 5, j1 = (c * kChunk + kChunk - 1) / 5;
+      // digits of bytes j0 .. j1 (at most three), 10 bits per byte
+      uint32_t dw = digits[seg[rr][j0]] | ((uint32_t)digits[seg[rr][j0 + 1]] << 10);
+      if (j1 > j0 + 1) dw |= (uint32_t)digits[seg[rr][j0 + 2]] << 20;
+      const int off = c * kChunk - 5 * j0;  // digit of weight 0 of the chunk
+      uint32_t pb = 0u, nb = 0u;
 #pragma unroll
       for (int b = 0; b < kChunk; ++b) {
-        const int64_t col = c * kChunk + b;
-        int v = src[col / 5];
-        const int q = (int)(col % 5);
-        for (int e = 0; e < q; ++e) v /= 3;
-        const int t = v % 3 - 1;
-        pb |= (uint32_t)(t > 0) << b;
-        nb |= (uint32_t)(t < 0) << b;
+        const uint32_t dg = (dw >> (2 * (off + b))) & 3u;  // t + 1
+        pb |= (uint32_t)(dg == 2u) << b;
+        nb |= (uint32_t)(dg == 0u) << b;
       }
+      cb[c * 32 + rr] = (uint8_t)pb;
+      cb[c * 32 + 16 + rr] = (uint8_t)nb;
     }
-    pos[r >> 2] |= pb << ((r & 3) * 8);
-    neg[r >> 2] |= nb << ((r & 3) * 8);
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(codes + (tile * chunks + c0) * 32);
+    for (int i = t; i < nc * 2; i += kBlock) dst[i] = cells[i];
   }
-  uint8_t* cell = codes + (tile * chunks + c) * 32;
-  *reinterpret_cast<uint4*>(cell) = make_uint4(pos[0], pos[1], pos[2], pos[3]);
-  *reinterpret_cast<uint4*>(cell + 16) = make_uint4(neg[0], neg[1], neg[2], neg[3]);
-  if (c % kChunksPerGroup == 0) {
-    const int64_t g = c / kChunksPerGroup;
-    uint16_t* dst = scales + (tile * groups + g) * kTileRows;
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-      const int64_t row = tile * kTileRows + r;
-      dst[r] = row < n ? in_scales[row * groups + g] : (uint16_t)0;
-    }
+  for (int i = t; i < kTileRows * groups; i += kBlock) {
+    const int rr = (int)(i / groups);
+    const int64_t g = i - (int64_t)rr * groups, rw = tile * kTileRows + rr;
+    scales[(tile * groups + g) * kTileRows + rr] = rw < n ? in_scales[rw * groups + g] : (uint16_t)0;
   }
 }
 
@@ -207,18 +258,17 @@ hipError_t launch_quantize_t2(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
 
 hipError_t launch_t2_to_base3(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                               uint8_t* out, uint16_t* out_scales, hipStream_t st) {
-  const int64_t work = n * ((k + 4) / 5);
-  int64_t blocks = (work + kBlock - 1) / kBlock;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(t2_to_base3_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, codes,
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL(t2_to_base3_kernel, dim3((unsigned)tiles), dim3(kBlock), 0, st, codes,
                      scales, n, k, out, out_scales);
   return hipGetLastError();
 }
 
 hipError_t launch_base3_to_t2(const uint8_t* in, const uint16_t* in_scales, int64_t n, int64_t k,
                               uint8_t* codes, uint16_t* scales, hipStream_t st) {
-  hipLaunchKernelGGL(base3_to_t2_kernel, tile_grid(n, k), dim3(kBlock), 0, st, in, in_scales, n, k,
-                     codes, scales);
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL(base3_to_t2_kernel, dim3((unsigned)tiles), dim3(kBlock), 0, st, in,
+                     in_scales, n, k, codes, scales);
   return hipGetLastError();
 }
 

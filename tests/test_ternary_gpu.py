@@ -87,7 +87,9 @@ def test_quantize_t2_full_lm_head_size():
     assert np.array_equal(host_u8(codes), oc)
 
 
-@pytest.mark.parametrize("n,k", [(16, 128), (37, 384), (5, 1280), (333, 640)])
+# (37, 2944): two whole 1280-weight blocks of the conversion kernels plus a
+# partial one, and 589 bytes per row (rows start at unaligned addresses)
+@pytest.mark.parametrize("n,k", [(16, 128), (37, 384), (5, 1280), (333, 640), (37, 2944)])
 def test_base3_round_trip_matches_oracle(n, k):
     import torch
 
