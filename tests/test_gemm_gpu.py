@@ -152,3 +152,17 @@ def test_full_pp512(fmt, m, n, k):
         ref = oracle.gemm(f, hc, hs, n, k, hx, m0=int(r), mrows=1)
         assert_close(yf[r:r + 1], ref, f"gemm full {fmt} row {r}")
         assert _bf16_ulp_ok(yb[r:r + 1], ref)
+
+
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+def test_max_k(fmt):
+    # the largest K the library accepts (2^22): 32768 K-groups, X rows of 8 MB
+    m, n, k = 3, 16, 1 << 22
+    say(f"gemm max k {fmt} m={m} n={n} k={k}")
+    g, codes, scales = _make(fmt, n, k, 4343)
+    x = synth.bf16_normal(g, (m, k))
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.gemm(f, codes, scales, n, k, x)
+    yf, yb = _run(fmt, codes, scales, n, k, x)
+    assert_close(yf, ref, f"gemm f32 {fmt} max k")
+    assert np.array_equal(yb, _rne_f32_to_bf16(yf))

@@ -144,3 +144,17 @@ def test_full_size(fmt, n, k, b):
         ref = np.concatenate([oracle.gemv(f, hc, hs, n, k, hx, row0=int(r0), nrows=1) for r0 in rows],
                              axis=1)
         assert_close(yh[:, rows], ref, f"full {fmt} {n}x{k} b={b} sampled rows")
+
+
+# the largest K the library accepts (2^22): 32768 groups, 4096 K-slices of
+# the table kernel, a 128 MB matrix-core workspace; offsets near 2^27 bytes
+@pytest.mark.parametrize("fmt,b", [("q1", 1), ("t2", 2), ("q1", 5)])
+def test_max_k(fmt, b):
+    n, k = 16, 1 << 22
+    say(f"gemv max k {fmt} n={n} k={k} b={b}")
+    g, codes, scales = _make(fmt, n, k, 4242 + b)
+    x = synth.fp16_normal(g, (b, k))
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.gemv(f, codes, scales, n, k, x)
+    y = _gemv(fmt, codes, scales, n, k, x)
+    assert_close(y, ref, f"{fmt} max k b={b}")
