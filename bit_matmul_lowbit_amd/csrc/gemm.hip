@@ -11,11 +11,13 @@
 // 32x32 blocks of the 32x32x16 BF16 matrix-core instruction.  The K loop
 // steps one scale group (128) at a time through LDS:
 //   * X[BM][128] BF16, the codes of W[BN][128] and the scales are loaded
-//     into registers groups ahead and written to LDS while the matrix cores
-//     work (a second LDS buffer for 128 x 128 tiles; one buffer and a
-//     three-stage register ring when each wave holds one 32 x 32 block), the
-//     codes expanded to exact BF16 {-1, 0, +1}.  The scale is NOT folded in:
-//     a BF16 scale would lose 3 of FP16's 11 significant bits;
+//     groups ahead and written to LDS while the matrix cores work (128 x 128
+//     tiles: a four-stage register ring and two LDS buffers; 32 x 32 blocks
+//     per wave: a two-stage ring, with one LDS buffer when three
+//     work-groups share a CU and two when the work-group runs alone, where
+//     the 128 x 96 kernel also loads X straight into LDS), the codes
+//     expanded to exact BF16 {-1, 0, +1}.  The scale is NOT folded in: a
+//     BF16 scale would lose 3 of FP16's 11 significant bits;
 //   * 8 k-steps of 16 accumulate the group's unscaled FP32 partial C_g, then
 //     C += s[n][g] * C_g in FP32 (one FMA per accumulator).
 // LDS rows are 256 B whose 16-byte slots are XOR-swizzled by the row index, so
