@@ -25,6 +25,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            kRawBufferFlags);
 }
 
+// Code-byte expansion helpers shared by the matrix-core GEMV and the GEMM.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// per-half shift of a packed pair of 16-bit values
+__device__ __forceinline__ uint32_t pk_shl(uint32_t d, uint32_t sh) {
+  const s16x2 a = __builtin_bit_cast(s16x2, d), s = __builtin_bit_cast(s16x2, sh);
+  return __builtin_bit_cast(uint32_t, (s16x2)(a << s));
+}
+
+// byte J of w in the low byte of both halves
+template <int J>
+__device__ __forceinline__ uint32_t rep_byte(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x0C000C00u | ((uint32_t)J << 16) | (uint32_t)J);
+}
+
+// shift that brings bits 2p and 2p + 1 of a byte placed in the low byte of
+// both halves to bits 15 and 31
+template <int P>
+constexpr uint32_t kPairShift = ((uint32_t)(14 - 2 * P) << 16) | (uint32_t)(15 - 2 * P);
+constexpr uint32_t kSignBits = 0x80008000u;
+
 // y[0 .. count) = 0 by the threads gid = 0, stride, 2 stride, ... of a grid:
 // 16-byte stores (y is 16-byte aligned), then the count % 4 tail.
 __device__ __forceinline__ void zero_f32(float* y, int64_t count, int64_t gid, int64_t stride) {

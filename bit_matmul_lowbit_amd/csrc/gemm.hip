@@ -42,25 +42,9 @@ __device__ __forceinline__ int slot(int r, int c) { return r * kRowU4 + (c ^ (r 
 
 // Code byte -> 8 BF16 values, two per dword (k = 2p in the low half, 2p + 1
 // in the high half).  Q1: the byte is placed in the low byte of both 16-bit
-// halves; a packed 16-bit shift by (15 - 2p, 14 - 2p) brings bits 2p and
-// 2p + 1 to bits 15 and 31, where v_bitop3 uses them as sign bits (+1 and
-// -1 differ only there): two VALU operations per dword.  Ternary: below.
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk_shl(uint32_t d, uint32_t sh) {
-  const s16x2 a = __builtin_bit_cast(s16x2, d), s = __builtin_bit_cast(s16x2, sh);
-  return __builtin_bit_cast(uint32_t, (s16x2)(a << s));
-}
-
-// byte J of w in the low byte of both halves
-template <int J>
-__device__ __forceinline__ uint32_t rep_byte(uint32_t w) {
-  return __builtin_amdgcn_perm(w, w, 0x0C000C00u | ((uint32_t)J << 16) | (uint32_t)J);
-}
-
-template <int P>
-constexpr uint32_t kPairShift = ((uint32_t)(14 - 2 * P) << 16) | (uint32_t)(15 - 2 * P);
-constexpr uint32_t kSignBits = 0x80008000u;
+// halves (rep_byte); a packed 16-bit shift by (15 - 2p, 14 - 2p) brings bits
+// 2p and 2p + 1 to bits 15 and 31, where v_bitop3 uses them as sign bits (+1
+// and -1 differ only there): two VALU operations per dword.  Ternary: below.
 constexpr uint32_t kOnes = 0x3F803F80u;  // BF16 +1 in both halves
 
 // Q1: bit 1 -> +1, bit 0 -> -1

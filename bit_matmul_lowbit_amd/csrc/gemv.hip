@@ -208,15 +208,8 @@ struct TileRegs {
 // Tile loads go through buffer resources whose base is the tile's row of
 // codes (or scales): the per-tile address arithmetic is scalar, the per-lane
 // offsets are fixed VGPRs, and a resource with zero length (used for tiles
-// past the end) returns zeros without touching memory.
-constexpr int kRawBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
-
+// past the end) returns zeros without touching memory (buffer_rsrc).
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
-                                           kRawBufferFlags);
-}
 
 // `off` is the per-lane (VGPR) offset, SOFF a constant added by the
 // instruction itself (no extra VGPR per cell)
@@ -345,7 +338,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
   const int64_t cstep = (int64_t)stride * cpitch, sstep = (int64_t)stride * spitch;
   auto load_next = [&](TileRegs<FMT>& r) {
     const bool in = tn < tb;
-    load_tile<FMT>(r, tile_rsrc(cn, in ? cpitch : 0), tile_rsrc(sn, in ? spitch : 0), coff, soff);
+    load_tile<FMT>(r, buffer_rsrc(cn, in ? cpitch : 0), buffer_rsrc(sn, in ? spitch : 0), coff, soff);
     tn += stride;
     cn += cstep;
     sn += sstep;
@@ -366,7 +359,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
     const int64_t bchunk = lane_chunk(s, bl % CH, CH, bq);
     const bool bvalid = bcol < b && bchunk < k / kChunk;
     const __amdgpu_buffer_rsrc_t xr =
-        tile_rsrc(reinterpret_cast<const uint8_t*>(xs), (int64_t)b * k * 2);
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(xs), (int64_t)b * k * 2);
     // an offset past the resource returns zeros
     const uint32_t xoff = bvalid ? (uint32_t)((bcol * k + bchunk * kChunk) * 2) : 0xFFFFFFF0u;
     xv4 = bload<0>(xr, xoff);

@@ -45,7 +45,6 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
@@ -54,12 +53,6 @@ constexpr int kSteps = 4;            // 32-k MFMA steps per 128-weight group
 constexpr int kXStep = 64 * 16;      // bytes of A operand per step (64 lanes x 16 B)
 constexpr int kRedPitch = 260;       // LDS pitch per batch row (256 rows + pad)
 
-constexpr int kRawBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRawBufferFlags);
-}
 
 template <int SOFF = 0>
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
@@ -67,29 +60,11 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// per-half shift of a packed pair of 16-bit values
-__device__ __forceinline__ uint32_t pk_shl(uint32_t d, uint32_t sh) {
-  const s16x2 a = __builtin_bit_cast(s16x2, d), s = __builtin_bit_cast(s16x2, sh);
-  return __builtin_bit_cast(uint32_t, (s16x2)(a << s));
-}
-
 // per-half arithmetic shift right by 15: 0xFFFF where bit 15 is set, else 0
 __device__ __forceinline__ uint32_t pk_mask15(uint32_t d) {
   const s16x2 a = __builtin_bit_cast(s16x2, d);
   return __builtin_bit_cast(uint32_t, (s16x2)(a >> (s16x2){15, 15}));
 }
-
-// byte J of w in the low byte of both halves
-template <int J>
-__device__ __forceinline__ uint32_t rep_byte(uint32_t w) {
-  return __builtin_amdgcn_perm(w, w, 0x0C000C00u | ((uint32_t)J << 16) | (uint32_t)J);
-}
-
-// shift that brings bits 2p and 2p + 1 to bits 15 and 31
-template <int P>
-constexpr uint32_t kPairShift = ((uint32_t)(14 - 2 * P) << 16) | (uint32_t)(15 - 2 * P);
-
-constexpr uint32_t kSignBits = 0x80008000u;
 
 // Q1: bit set -> +s, clear -> -s;  ss = s in both halves
 __device__ __forceinline__ f16x8 expand_q1(uint32_t d, uint32_t ss) {
@@ -223,8 +198,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   const uint32_t voff_c = (uint32_t)(tl * cpitch + q * (GB / 4));
   const uint32_t voff_s = (uint32_t)(tl * spitch);
   const uint32_t voff_x = (uint32_t)(lane * 16);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(xw, (int64_t)G * kSteps * kXStep);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(xw, 0);  // all loads return zero
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xw, (int64_t)G * kSteps * kXStep);
+  const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(xw, 0);  // all loads return zero
 
   // This work-group's items: blockIdx.x + i * gridDim.x.  Every wave runs
   // `per` group slots per item (slot i of an item is group
@@ -246,9 +221,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
     const bool live = sl < total && g < gend;
     const int64_t here = ntiles - T0 < 16 ? ntiles - T0 : 16;
     // lanes whose tile is past the end read past their resource: zeros
-    const __amdgpu_buffer_rsrc_t rc = rsrc(codes + T0 * cpitch, here * cpitch);
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + T0 * cpitch, here * cpitch);
     const __amdgpu_buffer_rsrc_t rs =
-        rsrc(reinterpret_cast<const uint8_t*>(scales) + T0 * spitch, here * spitch);
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(scales) + T0 * spitch, here * spitch);
     load_group<FMT>(r, live ? rc : rz, live ? rs : rz, live ? rx : rz, voff_c, voff_s, voff_x,
                     live ? g : 0);
   };
