@@ -46,6 +46,24 @@ template <int P>
 constexpr uint32_t kPairShift = ((uint32_t)(14 - 2 * P) << 16) | (uint32_t)(15 - 2 * P);
 constexpr uint32_t kSignBits = 0x80008000u;
 
+// SiLU(v) = v / (1 + e^-v) in FP32 with the device library's expf; for
+// v < -88 e^-v is infinite and the quotient is -0.
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// 8 FP16 values RNE(SiLU(g_j) * u_j) packed two per dword (j = 2p low half)
+__device__ __forceinline__ uint4 silu_mul8(const float (&gv)[8], const float (&uv)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // conversion to _Float16 rounds to nearest, ties to even
+    const _Float16 lo = (_Float16)(silu(gv[2 * p]) * uv[2 * p]);
+    const _Float16 hi = (_Float16)(silu(gv[2 * p + 1]) * uv[2 * p + 1]);
+    w[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // y[0 .. count) = 0 by the threads gid = 0, stride, 2 stride, ... of a grid:
 // 16-byte stores (y is 16-byte aligned), then the count % 4 tail.
 __device__ __forceinline__ void zero_f32(float* y, int64_t count, int64_t gid, int64_t stride) {
@@ -82,6 +100,14 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scale
 size_t gemv_workspace_bytes(int64_t k, int64_t b);
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st);
+// b < kMfmaMinBatch: the same, and a second range y2[0 .. n2) zeroed too
+hipError_t launch_gemv_prepare_zero2(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
+                                     void* ws, float* y2, int64_t n2, hipStream_t st);
+// b < kMfmaMinBatch: y += W z with z = RNE_fp16(SiLU(gate) * up) formed from
+// h (FP32 [b][2k], gate columns then up columns) inside the GEMV
+hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                       int64_t n, int64_t k, int64_t b, float* y, const float* h,
+                                       hipStream_t st);
 hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t* scales,
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st);

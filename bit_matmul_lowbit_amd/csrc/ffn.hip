@@ -10,21 +10,20 @@
 // SiLU(gate) * up is rounded to FP16, the activation type the down GEMV
 // reads.
 //
-// The chain is four launches on the caller's stream, none of which waits
-// on the host, so the caller can capture it in one HIP graph:
+// The chain runs on the caller's stream with no host wait, so the caller
+// can capture it in one HIP graph.  For b >= 3 (matrix-core GEMVs) it is
+// four launches:
 //   1. GEMV prepare: x -> workspace, h = 0
 //   2. GEMV accumulate: h += W_gu x                      (h FP32 [b][2f])
 //   3. silu_mul_kernel: z = RNE_fp16(SiLU(h_gate) * h_up), written straight
 //      into the down GEMV's workspace layout, and y = 0
 //   4. GEMV accumulate: y += W_dn z                      (y FP32 [b][k])
+// For b <= 2 (table GEMVs) step 1 also zeroes y, and step 4 forms z from h
+// in its table build (same arithmetic), so step 3 is not launched.
 #include "common.h"
 
 namespace lowbit {
 namespace {
-
-// SiLU(v) = v / (1 + e^-v) in FP32 with the device library's expf; for
-// v < -88 e^-v is infinite and the quotient is -0.
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 // One 16-byte vector of z: 8 consecutive FP16 values of batch row `row`
 // starting at column 8 * chunk; zeros for a row >= b.
@@ -36,16 +35,7 @@ __device__ __forceinline__ uint4 z_vector(const float* __restrict__ h, int64_t f
   const float4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
   const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
   const float uv[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-  uint32_t w[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    // conversion to _Float16 rounds to nearest, ties to even
-    const _Float16 lo = (_Float16)(silu(gv[2 * p]) * uv[2 * p]);
-    const _Float16 hi = (_Float16)(silu(gv[2 * p + 1]) * uv[2 * p + 1]);
-    w[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return silu_mul8(gv, uv);
 }
 
 // z in one of two layouts, and (optionally) y = 0:
@@ -117,11 +107,20 @@ hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scale
   void* ws_x = base;
   float* h = reinterpret_cast<float*>(base + align256((int64_t)gemv_workspace_bytes(k, b)));
   void* ws_z = reinterpret_cast<char*>(h) + align256(b * 2 * f * 4);
+  if (b < kMfmaMinBatch) {
+    // table GEMVs: the down GEMV forms z from h in its own table build, so
+    // the chain is three launches (prepare zeroes h and y)
+    hipError_t e = launch_gemv_prepare_zero2(2 * f, k, x, b, h, ws_x, y, b * k, st);
+    if (e != hipSuccess) return e;
+    e = launch_gemv_accumulate(fmt, gu_codes, gu_scales, 2 * f, k, b, h, ws_x, st);
+    if (e != hipSuccess) return e;
+    return launch_gemv_accumulate_silu(fmt, dn_codes, dn_scales, k, f, b, y, h, st);
+  }
   hipError_t e = launch_gemv_prepare(2 * f, k, x, b, h, ws_x, st);
   if (e != hipSuccess) return e;
   e = launch_gemv_accumulate(fmt, gu_codes, gu_scales, 2 * f, k, b, h, ws_x, st);
   if (e != hipSuccess) return e;
-  e = launch_silu(h, f, b, ws_z, b >= kMfmaMinBatch, y, b * k, st);
+  e = launch_silu(h, f, b, ws_z, true, y, b * k, st);
   if (e != hipSuccess) return e;
   return launch_gemv_accumulate(fmt, dn_codes, dn_scales, k, f, b, y, ws_z, st);
 }

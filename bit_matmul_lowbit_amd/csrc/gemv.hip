@@ -76,13 +76,16 @@ __device__ __forceinline__ int64_t lane_chunk(int64_t s, int lanec, int ch, int 
 }
 
 // prepare: x [b][k] -> workspace (read by the main kernel's table build), y = 0
+// (and y2 = 0 when given: the decode FFN zeroes its output here too)
 __global__ __launch_bounds__(kWG) void gemv_prepare_kernel(const uint4* __restrict__ x,
                                                            int64_t nvec, uint4* __restrict__ xs,
                                                            float* __restrict__ y,
-                                                           int64_t ycount) {
+                                                           int64_t ycount, float* __restrict__ y2,
+                                                           int64_t ycount2) {
   const int64_t gid = (int64_t)blockIdx.x * kWG + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kWG;
   zero_f32(y, ycount, gid, stride);
+  if (ycount2 > 0) zero_f32(y2, ycount2, gid, stride);
   for (int64_t i = gid; i < nvec; i += stride) xs[i] = x[i];
 }
 
@@ -296,11 +299,14 @@ __device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, int la
 // block index, so the chip sweeps the code plane front to back in one
 // contiguous front: HBM serves such a sweep measurably faster (about
 // 6.3 TB/s on MI355X) than hundreds of independent streams (about 4.8 TB/s).
-template <int FMT, int CH>
+// ZH: the activations are z = RNE_fp16(SiLU(gate) * up) of the decode FFN,
+// formed from h (FP32 [b][2k]: k gate columns, then k up columns) by the
+// table build itself (the same arithmetic as silu_mul_kernel).
+template <int FMT, int CH, bool ZH = false>
 __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ xs, float* __restrict__ y, int64_t n, int64_t k, int b,
-    int64_t ntiles, int64_t nslices) {
+    int64_t ntiles, int64_t nslices, const float* __restrict__ h) {
   __shared__ float4 table[kImages * kSliceFloats / 4];
   const int64_t s = blockIdx.x % nslices;
   const int64_t m = blockIdx.x / nslices;
@@ -358,11 +364,30 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
     const int bcol = bl / CH;
     const int64_t bchunk = lane_chunk(s, bl % CH, CH, bq);
     const bool bvalid = bcol < b && bchunk < k / kChunk;
-    const __amdgpu_buffer_rsrc_t xr =
-        buffer_rsrc(reinterpret_cast<const uint8_t*>(xs), (int64_t)b * k * 2);
-    // an offset past the resource returns zeros
-    const uint32_t xoff = bvalid ? (uint32_t)((bcol * k + bchunk * kChunk) * 2) : 0xFFFFFFF0u;
-    xv4 = bload<0>(xr, xoff);
+    if constexpr (!ZH) {
+      const __amdgpu_buffer_rsrc_t xr =
+          buffer_rsrc(reinterpret_cast<const uint8_t*>(xs), (int64_t)b * k * 2);
+      // an offset past the resource returns zeros
+      const uint32_t xoff = bvalid ? (uint32_t)((bcol * k + bchunk * kChunk) * 2) : 0xFFFFFFF0u;
+      xv4 = bload<0>(xr, xoff);
+    } else {
+      const __amdgpu_buffer_rsrc_t hr =
+          buffer_rsrc(reinterpret_cast<const uint8_t*>(h), (int64_t)b * 2 * k * 4);
+      const uint32_t go = bvalid ? (uint32_t)((bcol * 2 * k + bchunk * kChunk) * 4) : 0xFFFFFFE0u;
+      const uint32_t uo = bvalid ? go + (uint32_t)(k * 4) : 0xFFFFFFE0u;
+      const uint4 g0 = bload<0>(hr, go), g1 = bload<16>(hr, go);
+      const uint4 u0 = bload<0>(hr, uo), u1 = bload<16>(hr, uo);
+      // the build needs the product: wait for h here (see below for why the
+      // wave waits before its weight loads)
+      __asm__ volatile("" ::"v"(g0.x), "v"(g0.y), "v"(g0.z), "v"(g0.w), "v"(g1.x), "v"(g1.y),
+                       "v"(g1.z), "v"(g1.w), "v"(u0.x), "v"(u0.y), "v"(u0.z), "v"(u0.w), "v"(u1.x),
+                       "v"(u1.y), "v"(u1.z), "v"(u1.w));
+      const float gv[8] = {u2f(g0.x), u2f(g0.y), u2f(g0.z), u2f(g0.w),
+                           u2f(g1.x), u2f(g1.y), u2f(g1.z), u2f(g1.w)};
+      const float uv[8] = {u2f(u0.x), u2f(u0.y), u2f(u0.z), u2f(u0.w),
+                           u2f(u1.x), u2f(u1.y), u2f(u1.z), u2f(u1.w)};
+      xv4 = silu_mul8(gv, uv);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // an empty statement that reads xv4: the compiler waits for the load here
@@ -467,7 +492,7 @@ hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
                        int b, int64_t ntiles, int64_t nslices) {
 #define LOWBIT_LAUNCH(CHV)                                                                      \
   hipLaunchKernelGGL((gemv_main_kernel<FMT, CHV>), grid, dim3(kMainThreads), 0, st, codes,     \
-                     scales, xs, y, n, k, b, ntiles, nslices)
+                     scales, xs, y, n, k, b, ntiles, nslices, nullptr)
   switch (ch) {
     case 64: LOWBIT_LAUNCH(64); break;
     case 32: LOWBIT_LAUNCH(32); break;
@@ -494,7 +519,21 @@ hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t 
   int64_t blocks = (work + kWG - 1) / kWG;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(gemv_prepare_kernel, dim3((unsigned)blocks), dim3(kWG), 0, st,
-                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b);
+                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b,
+                     nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_prepare_zero2(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
+                                     void* ws, float* y2, int64_t n2, hipStream_t st) {
+  const int64_t nvec = b * k / 8;
+  const int64_t yvec = (n * b + n2 + 3) / 4;
+  const int64_t work = nvec > yvec ? nvec : yvec;
+  int64_t blocks = (work + kWG - 1) / kWG;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(gemv_prepare_kernel, dim3((unsigned)blocks), dim3(kWG), 0, st,
+                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b,
+                     y2, n2);
   return hipGetLastError();
 }
 
@@ -518,6 +557,31 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
   if (fmt == 1)
     return launch_main<1>(ch, grid, st, codes, scales, xs, y, n, k, (int)b, ntiles, nslices);
   return launch_main<2>(ch, grid, st, codes, scales, xs, y, n, k, (int)b, ntiles, nslices);
+}
+
+hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                       int64_t n, int64_t k, int64_t b, float* y, const float* h,
+                                       hipStream_t st) {
+  const int ch = kLanes / bp_for(b);  // 64 or 32: b <= 2
+  const int64_t nslices = nslices_for(k, ch);
+  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
+  int64_t G = (int64_t)cu_count() / nslices;
+  if (G < 1) G = 1;
+  const int64_t blocks = (ntiles + kMainWaves - 1) / kMainWaves;
+  if (G > blocks) G = blocks;
+  const dim3 grid((unsigned)(G * nslices));
+#define LOWBIT_LAUNCH(F, CHV)                                                                   \
+  hipLaunchKernelGGL((gemv_main_kernel<F, CHV, true>), grid, dim3(kMainThreads), 0, st, codes,  \
+                     scales, nullptr, y, n, k, (int)b, ntiles, nslices, h)
+  if (fmt == 1) {
+    if (ch == 64) LOWBIT_LAUNCH(1, 64);
+    else LOWBIT_LAUNCH(1, 32);
+  } else {
+    if (ch == 64) LOWBIT_LAUNCH(2, 64);
+    else LOWBIT_LAUNCH(2, 32);
+  }
+#undef LOWBIT_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace lowbit

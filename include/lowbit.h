@@ -267,6 +267,8 @@ size_t lowbit_ffn_workspace_bytes(int fmt, int64_t k, int64_t f, int64_t b);
  *   y_f32     : [b][k] FP32 (device, written)
  *   workspace : at least lowbit_ffn_workspace_bytes(fmt, k, f, b) bytes of
  *               device scratch, contents ignored on entry and clobbered.
+ * For b <= 2, z is formed inside the down GEMV (never written out) with the
+ * same arithmetic as lowbit_silu_mul.
  * Both matrices use format fmt; k and f must be multiples of 128.  As in
  * lowbit_gemv, K-slices are combined with atomic adds, so the last bits of
  * h and y may differ from run to run, and so may a z value that lies on an

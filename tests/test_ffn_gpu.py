@@ -81,7 +81,7 @@ def test_silu_mul_matches_oracle():
 
 
 SMALL = [(128, 128, 1), (256, 384, 2), (384, 256, 3), (512, 640, 5), (1024, 512, 8),
-         (256, 1024, 1), (640, 256, 4)]
+         (256, 1024, 1), (640, 256, 4), (2048, 6144, 2)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
@@ -106,12 +106,15 @@ def test_ffn_small_shapes(fmt, k, f, b):
     _ffn_ok(y.cpu().numpy(), ref, f"ffn {fmt} k={k} f={f} b={b}")
 
 
-def test_ffn_zero_gate_gives_exact_zeros():
+@pytest.mark.parametrize("b", [1, 2, 3])
+def test_ffn_zero_gate_gives_exact_zeros(b):
+    """SiLU(0) * up = 0 exactly, through both z paths (formed in the down
+    GEMV's table build for b <= 2, by its own launch for b >= 3)."""
     import torch
 
-    say("ffn zero gate")
-    g = synth.rng(2100)
-    k, f, b = 256, 256, 3
+    say(f"ffn zero gate b={b}")
+    g = synth.rng(2100 + b)
+    k, f = 256, 256
     t = synth.ternary(g, (2 * f, k))
     t[:f] = 0
     gu = oracle.t2_pack(t, synth.fp16_uniform(g, (2 * f, k // 128), 0.01, 0.2))
