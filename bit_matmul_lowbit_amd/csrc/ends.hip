@@ -93,18 +93,37 @@ __device__ __forceinline__ uint64_t block_max(uint64_t k, uint64_t* red) {
   return m;
 }
 
+// The best key of y[row][lo .. hi) (lo < hi) over a 256-thread work-group's
+// threads: four loads in flight per thread; an index past hi re-reads
+// element hi - 1, whose key is already a candidate.
+__device__ __forceinline__ uint64_t part_best(const float* __restrict__ y, int64_t row, int64_t n,
+                                              int64_t lo, int64_t hi) {
+  const float* yr = y + row * n;
+  uint64_t best = 0;  // below every real key (a value's ordered bits are >= 1)
+  for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += 4 * 256) {
+    float v[4];
+    int64_t ix[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ix[u] = i0 + u * 256 < hi ? i0 + u * 256 : hi - 1;
+      v[u] = yr[ix[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t kk = argmax_key(v[u], ix[u]);
+      best = kk > best ? kk : best;
+    }
+  }
+  return best;
+}
+
 // phase 1: work-group (p, row) reduces part p of batch row `row` to a key
 __global__ __launch_bounds__(256) void argmax_part_kernel(const float* __restrict__ y, int64_t n,
                                                           int64_t per, uint64_t* __restrict__ part) {
   __shared__ uint64_t red[4];
   const int64_t p = blockIdx.x, row = blockIdx.y;
   const int64_t lo = p * per, hi = lo + per < n ? lo + per : n;
-  uint64_t best = 0;  // below every real key (a value's ordered bits are >= 1)
-  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-    const uint64_t kk = argmax_key(y[row * n + i], i);
-    best = kk > best ? kk : best;
-  }
-  best = block_max(best, red);
+  uint64_t best = block_max(part_best(y, row, n, lo, hi), red);
   if (threadIdx.x == 0) part[row * gridDim.x + p] = best;
 }
 
@@ -131,7 +150,9 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restri
 constexpr int kArgmaxParts = 256;
 
 int argmax_parts(int64_t n) {
-  // parts of at least 1024 elements, at most kArgmaxParts of them
+  // parts of at least 1024 elements, at most kArgmaxParts of them; with
+  // per = ceil(n / parts) every part is non-empty, since parts * (parts - 1)
+  // < n
   int64_t p = (n + 1023) / 1024;
   return (int)(p < 1 ? 1 : (p > kArgmaxParts ? kArgmaxParts : p));
 }

@@ -121,3 +121,28 @@ def test_lm_head_top1(fmt, n, k, b):
         assert ref[i, idx[i]] >= top[1] - err
         if top[1] - top[0] > err:
             assert idx[i] == np.argmax(ref[i])
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [("t2", 37, 256, 1), ("q1", 5000, 384, 2), ("q1", 1500, 128, 3),
+                                       ("t2", 5000, 256, 8), ("q1", 262160, 128, 1)])
+def test_lm_head_reused_workspace(fmt, n, k, b):
+    """The workspace's contents are ignored on entry: with a workspace full
+    of 0xFF, and again on a second call that finds the first call's
+    leftovers, the logits follow the GEMV bound and the index is the argmax
+    of the logits the call returned.  Shapes cover one argmax part, several,
+    the 256-part cap, and both GEMV kernels (b <= 2 and b >= 3)."""
+    import torch
+
+    say(f"lm head reused workspace {fmt} n={n} k={k} b={b}")
+    codes, scales, hc, hs = full_weights(fmt, n, k, 1900 + b)
+    ws = torch.full((lowbit.lowbit_lm_head_workspace_bytes(fmt, n, k, b),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    of = oracle.Q1 if fmt == "q1" else oracle.T2
+    for call in range(2):
+        x = synth.dev_fp16_normal((b, k), 1.0, 1910 + 10 * b + call)
+        y, idx, val = lowbit.lowbit_lm_head(fmt, codes, scales, n, k, x, workspace=ws)
+        torch.cuda.synchronize()
+        y, idx, val = y.cpu().numpy(), idx.cpu().numpy(), val.cpu().numpy()
+        assert_close(y, oracle.gemv(of, hc, hs, n, k, host_u16(x)), f"lm head logits call {call}")
+        assert np.array_equal(idx, np.argmax(y, axis=1)), (call, idx)
+        assert np.array_equal(val, y[np.arange(b), idx]), call
