@@ -58,8 +58,18 @@ def log(*a):
 
 
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Fingerprint of a kernel source's code: sha256 prefix of the text with
+    comments removed and whitespace collapsed, so that the recorded HBM
+    counters stay valid across comment-only edits and lapse on any change
+    to the code itself."""
+    import re
+
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------

@@ -30,6 +30,11 @@
 //      rows' scales, reduced over the groups, and added to y with one FP32
 //      atomic per row and K-slice.
 //
+// A second entry (launch_gemv_accumulate_silu, b <= 2) serves the decode
+// FFN's down projection: its activations z = RNE_fp16(SiLU(gate) * up) are
+// formed from the FP32 gate+up result h while the tables are built, so z is
+// never written out.
+//
 // With batch b > 1 the 64 lanes are split into BP = 2, 4, 8 column groups of
 // CH = 64 / BP lanes (BP = b rounded up to a power of two); the code cells
 // are then re-read by each column group from cache, and the VALU work grows
