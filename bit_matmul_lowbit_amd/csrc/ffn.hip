@@ -94,10 +94,10 @@ hipError_t launch_silu_mul(const float* h, int64_t f, int64_t b, uint16_t* z, hi
 }
 
 // workspace: [x prepared for W_gu][h FP32 b x 2f][z prepared for W_dn], each
-// part 256-byte aligned
+// part 256-byte aligned; b < kMfmaMinBatch never writes z out, so has no z part
 size_t ffn_workspace_bytes(int64_t k, int64_t f, int64_t b) {
   return (size_t)(align256((int64_t)gemv_workspace_bytes(k, b)) + align256(b * 2 * f * 4) +
-                  align256((int64_t)gemv_workspace_bytes(f, b)));
+                  (b >= kMfmaMinBatch ? align256((int64_t)gemv_workspace_bytes(f, b)) : 0));
 }
 
 hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scales,
@@ -106,7 +106,6 @@ hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scale
   char* base = static_cast<char*>(ws);
   void* ws_x = base;
   float* h = reinterpret_cast<float*>(base + align256((int64_t)gemv_workspace_bytes(k, b)));
-  void* ws_z = reinterpret_cast<char*>(h) + align256(b * 2 * f * 4);
   if (b < kMfmaMinBatch) {
     // table GEMVs: the down GEMV forms z from h in its own table build, so
     // the chain is three launches (prepare zeroes h and y)
@@ -116,6 +115,7 @@ hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scale
     if (e != hipSuccess) return e;
     return launch_gemv_accumulate_silu(fmt, dn_codes, dn_scales, k, f, b, y, h, st);
   }
+  void* ws_z = reinterpret_cast<char*>(h) + align256(b * 2 * f * 4);
   hipError_t e = launch_gemv_prepare(2 * f, k, x, b, h, ws_x, st);
   if (e != hipSuccess) return e;
   e = launch_gemv_accumulate(fmt, gu_codes, gu_scales, 2 * f, k, b, h, ws_x, st);

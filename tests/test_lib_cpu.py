@@ -135,11 +135,12 @@ def test_validation_returns_before_launch(lib):
 def test_ffn_workspace_query_and_validation(lib):
     def a256(v):
         return (v + 255) // 256 * 256
-    # [x prepared for W_gu][h FP32 b x 2f][z prepared for W_dn], 256-aligned parts
+    # [x prepared for W_gu][h FP32 b x 2f][z prepared for W_dn], 256-aligned
+    # parts; b <= 2 forms z inside the down GEMV and has no z part
     for b in (1, 2, 5, 8):
         for k, f in ((5120, 17408), (2048, 6144), (128, 128)):
             want = (a256(lowbit.lowbit_gemv_workspace_bytes("q1", 2 * f, k, b)) + a256(b * 2 * f * 4)
-                    + a256(lowbit.lowbit_gemv_workspace_bytes("q1", k, f, b)))
+                    + (a256(lowbit.lowbit_gemv_workspace_bytes("q1", k, f, b)) if b >= 3 else 0))
             assert lowbit.lowbit_ffn_workspace_bytes("q1", k, f, b) == want
     assert lowbit.lowbit_ffn_workspace_bytes("q1", 5120, 100, 1) == 0   # f % 128
     assert lowbit.lowbit_ffn_workspace_bytes("q1", 5000, 128, 1) == 0   # k % 128
