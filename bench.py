@@ -473,9 +473,16 @@ def main():
     ap.add_argument("--workload", default="t2_lmhead_152k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="all",
+                    help="comma-separated secondary groups to run: gemv, quantize, ffn, "
+                         "ternary, ends, gemm (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    groups = {"gemv", "quantize", "ffn", "ternary", "ends", "gemm"}
+    chosen = groups if args.secondary == "all" else set(args.secondary.split(","))
+    if not chosen <= groups:
+        ap.error(f"--secondary: unknown group(s) {sorted(chosen - groups)}")
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported",
@@ -550,7 +557,7 @@ def main():
             "t2_ffn_1p7b_down_2048x6144_b1": ("t2", 2048, 6144, 1001),
             "q1_ffn_27b_gateup_34816x5120": ("q1", 34816, 5120, 1002),
             "q1_ffn_27b_down_5120x17408": ("q1", 5120, 17408, 1002),
-        }.items():
+        }.items() if "gemv" in chosen else ():
             for b2 in ([1, 2, 5, 8] if "27b" in name else [1]):
                 key = name if "27b" not in name else f"{name}_b{b2}"
                 rr = time_gemv(f2, n2, k2, b2, seeds, 50, 10, with_graph=True)
@@ -559,22 +566,26 @@ def main():
                             "graph_us_per_step": round(rr["graph_ms_per_step"] * 1e3, 2),
                             "graph_gbs": round(rr["weight_bytes"] / (rr["graph_ms_per_step"] * 1e-3) / 1e9, 1)}
                 log(f"[bench] {key}: {sec[key]}")
-        q = time_quantize(151936, 5120, 1003, 20, 3)
-        sec["q1_quantize_151936x5120"] = {"gbs": round(q["gbs"], 1), "us": round(q["ms"] * 1e3, 1),
-                                          "bytes_moved": q["bytes_moved"]}
-        log(f"[bench] quantize: {sec['q1_quantize_151936x5120']}")
+        if "quantize" in chosen:
+            q = time_quantize(151936, 5120, 1003, 20, 3)
+            sec["q1_quantize_151936x5120"] = {"gbs": round(q["gbs"], 1), "us": round(q["ms"] * 1e3, 1),
+                                              "bytes_moved": q["bytes_moved"]}
+            log(f"[bench] quantize: {sec['q1_quantize_151936x5120']}")
         for key, (ff, kf, fff, bf) in {
                 "ffn_q1_27b_k5120_f17408_b1": ("q1", 5120, 17408, 1),
                 "ffn_q1_27b_k5120_f17408_b5": ("q1", 5120, 17408, 5),
-                "ffn_t2_1p7b_k2048_f6144_b1": ("t2", 2048, 6144, 1)}.items():
+                "ffn_t2_1p7b_k2048_f6144_b1": ("t2", 2048, 6144, 1)}.items() if "ffn" in chosen else ():
             sec[key] = time_ffn(ff, kf, fff, bf, 1100 + fff + bf, 30, 5)
             log(f"[bench] {key}: {sec[key]}")
-        sec["ternary_151936x5120"] = time_ternary(151936, 5120, 1950)
-        log(f"[bench] ternary_151936x5120: {sec['ternary_151936x5120']}")
-        sec["ends_t2_151936x5120_b1"] = time_ends(151936, 5120, 1900)
-        log(f"[bench] ends_t2_151936x5120_b1: {sec['ends_t2_151936x5120_b1']}")
+        if "ternary" in chosen:
+            sec["ternary_151936x5120"] = time_ternary(151936, 5120, 1950)
+            log(f"[bench] ternary_151936x5120: {sec['ternary_151936x5120']}")
+        if "ends" in chosen:
+            sec["ends_t2_151936x5120_b1"] = time_ends(151936, 5120, 1900)
+            log(f"[bench] ends_t2_151936x5120_b1: {sec['ends_t2_151936x5120_b1']}")
         for key, (f2, m2, n2, k2) in {"gemm_pp512_t2_512x6144x2048": ("t2", 512, 6144, 2048),
-                                       "gemm_pp512_q1_512x2048x6144": ("q1", 512, 2048, 6144)}.items():
+                                       "gemm_pp512_q1_512x2048x6144": ("q1", 512, 2048, 6144)}.items() \
+                if "gemm" in chosen else ():
             g = time_gemm(f2, m2, n2, k2, 1004 + n2, 50, 10)
             sec[key] = {"tflops": round(g["tflops"], 2), "us": round(g["ms"] * 1e3, 2),
                         "frac_bf16_peak": round(g["frac_bf16_peak"], 4),
