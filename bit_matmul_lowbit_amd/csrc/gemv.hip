@@ -382,8 +382,8 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
       const uint32_t uo = bvalid ? go + (uint32_t)(k * 4) : 0xFFFFFFE0u;
       const uint4 g0 = bload<0>(hr, go), g1 = bload<16>(hr, go);
       const uint4 u0 = bload<0>(hr, uo), u1 = bload<16>(hr, uo);
-      // the build needs the product: wait for h here (see below for why the
-      // wave waits before its weight loads)
+      // the build needs the product: wait for h here, before any weight
+      // load goes out (as for x above)
       __asm__ volatile("" ::"v"(g0.x), "v"(g0.y), "v"(g0.z), "v"(g0.w), "v"(g1.x), "v"(g1.y),
                        "v"(g1.z), "v"(g1.w), "v"(u0.x), "v"(u0.y), "v"(u0.z), "v"(u0.w), "v"(u1.x),
                        "v"(u1.y), "v"(u1.z), "v"(u1.w));
