@@ -73,6 +73,10 @@ __device__ __forceinline__ void zero_f32(float* y, int64_t count, int64_t gid, i
   if (gid < count - nv * 4) y[nv * 4 + gid] = 0.0f;
 }
 
+// Compute units of the current device (256 if it cannot be queried), cached
+// per device id; safe to call from several host threads.
+int device_cu_count();
+
 // Kernel launchers (host side, defined in the .hip files).  All return a
 // hipError_t from the launch; shapes were validated by the caller.
 hipError_t launch_quantize_q1(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,

@@ -588,19 +588,6 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     }
 }
 
-int cu_count_gemm() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 template <int FMT, int BM, int BN, int KT, int WM = 2, int WN = 2>
 hipError_t launch_tile(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                        const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
@@ -621,20 +608,20 @@ hipError_t launch_fmt(const uint8_t* codes, const uint16_t* scales, int64_t n, i
   // 128 x 128 tiles when there are enough of them for two per CU, otherwise
   // 64 x 64 tiles (4x as many work-groups)
   const int64_t big = ((n + 127) / 128) * ((m + 127) / 128);
-  if (big >= 2 * (int64_t)cu_count_gemm())
+  if (big >= 2 * (int64_t)device_cu_count())
     return launch_tile<FMT, 128, 128, 1>(codes, scales, n, k, x, m, y, out_f32, st);
   // 128 x 96 tiles of twelve 32 x 32 waves (one work-group per CU, three
   // waves per SIMD) when they fill whole rounds of the CUs: each W row is
   // expanded once per 128 rows of X instead of 64, and a tile re-reads less
   // from LDS per MFMA than four 64 x 64 ones
-  const int64_t cus = (int64_t)cu_count_gemm();
+  const int64_t cus = (int64_t)device_cu_count();
   const int64_t t96 = ((n + 95) / 96) * ((m + 127) / 128);
   if (m >= 128 && t96 >= cus && t96 % cus == 0)
     return launch_tile<FMT, 128, 96, 1, 4, 3>(codes, scales, n, k, x, m, y, out_f32, st);
   // with no more 64 x 64 tiles than CUs, two K-teams per tile (one 8-wave
   // work-group per CU) keep twice as many waves busy
   const int64_t small = ((n + 63) / 64) * ((m + 63) / 64);
-  if (small <= (int64_t)cu_count_gemm() && k >= 2 * BK)
+  if (small <= (int64_t)device_cu_count() && k >= 2 * BK)
     return launch_tile<FMT, 64, 64, 2>(codes, scales, n, k, x, m, y, out_f32, st);
   return launch_tile<FMT, 64, 64, 1>(codes, scales, n, k, x, m, y, out_f32, st);
 }

@@ -477,20 +477,6 @@ int64_t nslices_for(int64_t k, int ch) {
   return (chunks + 2 * ch - 1) / (2 * ch);
 }
 
-// compute units of the current device (cached per device id)
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 template <int FMT>
 hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
                        const uint16_t* scales, const uint16_t* xs, float* y, int64_t n, int64_t k,
@@ -546,14 +532,14 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st) {
   if (b >= kMfmaMinBatch)
-    return launch_gemv_mfma(fmt, codes, scales, n, k, b, y, ws, cu_count(), st);
+    return launch_gemv_mfma(fmt, codes, scales, n, k, b, y, ws, device_cu_count(), st);
   const int ch = kLanes / bp_for(b);
   const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
   const uint16_t* xs = static_cast<const uint16_t*>(ws);
   // G work-groups per slice: about one per CU in all, and no more than there
   // are 16-tile blocks
-  int64_t G = (int64_t)cu_count() / nslices;
+  int64_t G = (int64_t)device_cu_count() / nslices;
   if (G < 1) G = 1;
   const int64_t blocks = (ntiles + kMainWaves - 1) / kMainWaves;
   if (G > blocks) G = blocks;
@@ -570,7 +556,7 @@ hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint
   const int ch = kLanes / bp_for(b);  // 64 or 32: b <= 2
   const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
-  int64_t G = (int64_t)cu_count() / nslices;
+  int64_t G = (int64_t)device_cu_count() / nslices;
   if (G < 1) G = 1;
   const int64_t blocks = (ntiles + kMainWaves - 1) / kMainWaves;
   if (G > blocks) G = blocks;

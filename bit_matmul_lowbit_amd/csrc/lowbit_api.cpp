@@ -4,6 +4,28 @@
 
 #include "common.h"
 
+#include <atomic>
+
+namespace lowbit {
+
+int device_cu_count() {
+  // atomics: first calls may race from several host threads (they store the
+  // same value)
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+}  // namespace lowbit
+
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
