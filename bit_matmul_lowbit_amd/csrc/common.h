@@ -50,14 +50,26 @@ constexpr uint32_t kSignBits = 0x80008000u;
 // v < -88 e^-v is infinite and the quotient is -0.
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
-// 8 FP16 values RNE(SiLU(g_j) * u_j) packed two per dword (j = 2p low half)
+// The FP32 product a * b rounded to FP16 (nearest-even), IEEE in every
+// case including the sign of a zero.  Written plainly, the compiler turns a
+// product followed by the FP16 conversion into one mixed-precision FMA with
+// a +0 addend (v_fma_mixlo_f16 a, b, 0), and -0 + +0 is +0: a product that
+// is -0 (SiLU(v) = -0 for v < -88, times u > 0) came out as +0.  The empty
+// asm statement keeps the product in its own v_mul_f32, converted by
+// v_cvt_f16_f32.
+__device__ __forceinline__ _Float16 mul_to_fp16(float a, float b) {
+  float p = a * b;
+  __asm__("" : "+v"(p));
+  return (_Float16)p;
+}
+
+// 8 FP16 values RNE_fp16(SiLU(g_j) * u_j) packed two per dword (j = 2p low half)
 __device__ __forceinline__ uint4 silu_mul8(const float (&gv)[8], const float (&uv)[8]) {
   uint32_t w[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    // conversion to _Float16 rounds to nearest, ties to even
-    const _Float16 lo = (_Float16)(silu(gv[2 * p]) * uv[2 * p]);
-    const _Float16 hi = (_Float16)(silu(gv[2 * p + 1]) * uv[2 * p + 1]);
+    const _Float16 lo = mul_to_fp16(silu(gv[2 * p]), uv[2 * p]);
+    const _Float16 hi = mul_to_fp16(silu(gv[2 * p + 1]), uv[2 * p + 1]);
     w[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }

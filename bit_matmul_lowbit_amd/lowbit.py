@@ -120,6 +120,29 @@ def _dev(t, dtypes, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need_numel(t, count, name):
+    """t must hold at least `count` elements (the C interface takes no buffer
+    lengths, so a short buffer would be read or written past its end)."""
+    if t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {count}")
+
+
+def _need_shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _need_planes(fmt, n, k, codes, scales, what=""):
+    """codes / scales large enough for an n x k matrix in `fmt` (layout v1).
+    An invalid shape is left to the library, which rejects it."""
+    cb = lowbit_codes_bytes(fmt, n, k)
+    sb = lowbit_scales_bytes(fmt, n, k)
+    if cb:
+        _need_numel(codes, cb, what + "codes")
+    if sb:
+        _need_numel(scales, sb // 2, what + "scales")
+
+
 # ---------------------------------------------------------------------------
 # host-only queries
 
@@ -159,6 +182,7 @@ def lowbit_quantize_q1(w, codes=None, scales=None, stream=None):
     n, k = w.shape
     wp = _dev(w, (torch.float16,), "w")
     codes, scales = _planes(LOWBIT_FMT_Q1_G128, n, k, w.device, codes, scales)
+    _need_planes(LOWBIT_FMT_Q1_G128, n, k, codes, scales)
     _check(load().lowbit_quantize_q1(wp, n, k, _dev(codes, (torch.uint8,), "codes"),
                                      _dev(scales, (torch.float16, torch.int16), "scales"),
                                      _stream(stream)), "lowbit_quantize_q1")
@@ -175,6 +199,7 @@ def lowbit_pack_t2(t, s, codes=None, scales=None, stream=None):
     if tuple(s.shape) != (n, k // 128):
         raise ValueError("s must be [n][k/128]")
     codes, scales = _planes(LOWBIT_FMT_T2_G128, n, k, t.device, codes, scales)
+    _need_planes(LOWBIT_FMT_T2_G128, n, k, codes, scales)
     _check(load().lowbit_pack_t2(tp, sp, n, k, _dev(codes, (torch.uint8,), "codes"),
                                  _dev(scales, (torch.float16, torch.int16), "scales"),
                                  _stream(stream)), "lowbit_pack_t2")
@@ -193,8 +218,10 @@ def lowbit_unpack(fmt, codes, scales, n: int, k: int, out=None, stream=None):
     """codes + scales -> dense FP16 [n][k]."""
     import torch
 
+    _need_planes(fmt, n, k, codes, scales)
     if out is None:
         out = torch.empty((n, k), dtype=torch.float16, device=codes.device)
+    _need_shape(out, (n, k), "out")
     _check(load().lowbit_unpack(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
                                 _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
                                 _dev(out, (torch.float16, torch.int16), "out"), _stream(stream)),
@@ -210,8 +237,10 @@ def lowbit_gemv(fmt, codes, scales, n: int, k: int, x, out=None, workspace=None,
     b = x2.shape[0]
     if x2.shape[1] != k:
         raise ValueError("x must have k columns")
+    _need_planes(fmt, n, k, codes, scales)
     if out is None:
         out = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _need_numel(out, b * n, "out")
     need = lowbit_gemv_workspace_bytes(fmt, n, k, b)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
@@ -230,6 +259,9 @@ def lowbit_gemv_prepare(n: int, k: int, x, out, workspace, stream=None):
 
     x2 = x if x.dim() == 2 else x.view(1, -1)
     b = x2.shape[0]
+    if x2.shape[1] != k:
+        raise ValueError("x must have k columns")
+    _need_numel(out, b * n, "out")
     _check(load().lowbit_gemv_prepare(n, k, _dev(x2, (torch.float16,), "x"), b,
                                       _dev(out, (torch.float32,), "out"),
                                       _dev(workspace, (torch.uint8,), "workspace"),
@@ -242,6 +274,8 @@ def lowbit_gemv_accumulate(fmt, codes, scales, n: int, k: int, b: int, out, work
     """out FP32 [b][n] += W.x with the tables left by lowbit_gemv_prepare."""
     import torch
 
+    _need_planes(fmt, n, k, codes, scales)
+    _need_numel(out, b * n, "out")
     _check(load().lowbit_gemv_accumulate(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
                                          _dev(scales, (torch.float16, torch.int16), "scales"),
                                          n, k, b, _dev(out, (torch.float32,), "out"),
@@ -255,9 +289,13 @@ def lowbit_gemm(fmt, codes, scales, n: int, k: int, x, out=None, stream=None):
     """X BF16 [m][k] -> Y BF16 [m][n]."""
     import torch
 
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
     m = x.shape[0]
+    _need_planes(fmt, n, k, codes, scales)
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _need_numel(out, m * n, "out")
     _check(load().lowbit_gemm(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
                               _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
                               _dev(x, (torch.bfloat16,), "x"), m,
@@ -269,9 +307,13 @@ def lowbit_gemm_f32(fmt, codes, scales, n: int, k: int, x, out=None, stream=None
     """X BF16 [m][k] -> Y FP32 [m][n] (same contraction, unrounded store)."""
     import torch
 
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
     m = x.shape[0]
+    _need_planes(fmt, n, k, codes, scales)
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _need_numel(out, m * n, "out")
     _check(load().lowbit_gemm_f32(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
                                   _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
                                   _dev(x, (torch.bfloat16,), "x"), m,
@@ -291,6 +333,7 @@ def lowbit_silu_mul(h, out=None, stream=None):
     f = f2 // 2
     if out is None:
         out = torch.empty((b, f), dtype=torch.float16, device=h.device)
+    _need_numel(out, b * f, "out")
     _check(load().lowbit_silu_mul(_dev(h2, (torch.float32,), "h"), f, b,
                                   _dev(out, (torch.float16,), "out"), _stream(stream)),
            "lowbit_silu_mul")
@@ -311,8 +354,11 @@ def lowbit_ffn(fmt, gu_codes, gu_scales, dn_codes, dn_scales, k: int, f: int, x,
     b = x2.shape[0]
     if x2.shape[1] != k:
         raise ValueError("x must have k columns")
+    _need_planes(fmt, 2 * f, k, gu_codes, gu_scales, "gu_")
+    _need_planes(fmt, k, f, dn_codes, dn_scales, "dn_")
     if out is None:
         out = torch.empty((b, k), dtype=torch.float32, device=x.device)
+    _need_numel(out, b * k, "out")
     need = lowbit_ffn_workspace_bytes(fmt, k, f, b)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
@@ -332,8 +378,10 @@ def lowbit_embed(fmt, codes, scales, n: int, k: int, ids, out=None, stream=None)
     import torch
 
     count = ids.numel()
+    _need_planes(fmt, n, k, codes, scales)
     if out is None:
         out = torch.empty((count, k), dtype=torch.float16, device=ids.device)
+    _need_numel(out, count * k, "out")
     _check(load().lowbit_embed(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
                                _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
                                _dev(ids, (torch.int32,), "ids"), count,
@@ -352,6 +400,8 @@ def lowbit_argmax(y, idx=None, val=None, workspace=None, stream=None):
         idx = torch.empty(b, dtype=torch.int32, device=y.device)
     if val is None:
         val = torch.empty(b, dtype=torch.float32, device=y.device)
+    _need_numel(idx, b, "idx")
+    _need_numel(val, b, "val")
     need = int(load().lowbit_argmax_workspace_bytes(n, b))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=y.device)
@@ -373,12 +423,18 @@ def lowbit_lm_head(fmt, codes, scales, n: int, k: int, x, out=None, idx=None, va
 
     x2 = x if x.dim() == 2 else x.view(1, -1)
     b = x2.shape[0]
+    if x2.shape[1] != k:
+        raise ValueError("x must have k columns")
+    _need_planes(fmt, n, k, codes, scales)
     if out is None:
         out = torch.empty((b, n), dtype=torch.float32, device=x.device)
     if idx is None:
         idx = torch.empty(b, dtype=torch.int32, device=x.device)
     if val is None:
         val = torch.empty(b, dtype=torch.float32, device=x.device)
+    _need_numel(out, b * n, "out")
+    _need_numel(idx, b, "idx")
+    _need_numel(val, b, "val")
     need = lowbit_lm_head_workspace_bytes(fmt, n, k, b)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
@@ -398,6 +454,7 @@ def lowbit_quantize_t2(w, codes=None, scales=None, stream=None):
 
     n, k = w.shape
     codes, scales = _planes("t2", n, k, w.device, codes, scales)
+    _need_planes("t2", n, k, codes, scales)
     _check(load().lowbit_quantize_t2(_dev(w, (torch.float16,), "w"), n, k,
                                      _dev(codes, (torch.uint8,), "codes"),
                                      _dev(scales, (torch.float16, torch.int16), "scales"),
@@ -413,6 +470,9 @@ def lowbit_t2_to_base3(codes, scales, n: int, k: int, out=None, out_scales=None,
         out = torch.empty((n, (k + 4) // 5), dtype=torch.uint8, device=codes.device)
     if out_scales is None:
         out_scales = torch.empty((n, k // 128), dtype=torch.float16, device=codes.device)
+    _need_planes("t2", n, k, codes, scales)
+    _need_numel(out, n * ((k + 4) // 5), "out")
+    _need_numel(out_scales, n * (k // 128), "out_scales")
     _check(load().lowbit_t2_to_base3(_dev(codes, (torch.uint8,), "codes"),
                                      _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
                                      _dev(out, (torch.uint8,), "out"),
@@ -426,6 +486,9 @@ def lowbit_base3_to_t2(b3, scales_rm, n: int, k: int, codes=None, scales=None, s
     import torch
 
     codes, scales = _planes("t2", n, k, b3.device, codes, scales)
+    _need_planes("t2", n, k, codes, scales)
+    _need_numel(b3, n * ((k + 4) // 5), "b3")
+    _need_numel(scales_rm, n * (k // 128), "scales_rm")
     _check(load().lowbit_base3_to_t2(_dev(b3, (torch.uint8,), "b3"),
                                      _dev(scales_rm, (torch.float16, torch.int16), "scales_rm"),
                                      n, k, _dev(codes, (torch.uint8,), "codes"),

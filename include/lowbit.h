@@ -63,6 +63,12 @@
  *   - Pointers are HIP device pointers unless stated otherwise; the caller
  *     allocates and frees every buffer.  The library never allocates,
  *     frees or synchronises, and keeps no state between calls.
+ *   - Outputs that kernels accumulate with FP32 atomic adds -- y of
+ *     lowbit_gemv, lowbit_gemv_accumulate, lowbit_ffn and lowbit_lm_head,
+ *     and the FFN's h in its workspace -- must be coarse-grained device
+ *     memory (hipMalloc, or torch's CUDA allocator).  The library is built
+ *     with -munsafe-fp-atomics: on fine-grained or host-coherent memory
+ *     such adds may be lost.
  *   - FP16 and BF16 values are passed as their 16-bit patterns (uint16_t).
  *   - Every call validates its arguments on the host, then enqueues its
  *     kernels on `stream` and returns without waiting.  On a validation
@@ -110,7 +116,10 @@ int lowbit_version(void);
 /* Human-readable name of a status code; never NULL. */
 const char* lowbit_status_str(int status);
 
-/* Bytes of the code plane / scale plane for an n x k matrix in `fmt`.
+/* Bytes of the code plane / scale plane for an n x k matrix in `fmt`
+ * [P1 s.7: one bit per weight and one FP16 scale per 128 weights, 18 B per
+ * group; P2 "Como funciona la compresion": ternary codes with one FP16
+ * scale per group of 128, here two bits per weight, 34 B per group].
  * Q1: Np*k/8, T2: Np*k/4, scales: Np*(k/128)*2, with Np = n rounded up to 16.
  * Returns 0 for an invalid format or shape.  Host-only; touches no GPU. */
 size_t lowbit_codes_bytes(int fmt, int64_t n, int64_t k);
@@ -139,8 +148,10 @@ int lowbit_pack_t2(const int8_t* t, const uint16_t* s_fp16, int64_t n,
                    int64_t k, void* codes, uint16_t* scales,
                    hipStream_t stream);
 
-/* Generic pack entry: Q1 -> lowbit_quantize_q1(src as FP16, src_scales must be
- * NULL); T2 -> lowbit_pack_t2(src as int8, src_scales as FP16). */
+/* Generic pack entry  [P1 s.7 for Q1, P2 "Como funciona la compresion" for
+ * ternary]: Q1 -> lowbit_quantize_q1(src as FP16, src_scales must be NULL);
+ * T2 -> lowbit_pack_t2(src as int8, src_scales as FP16).  Same arguments,
+ * layouts and errors as the call it forwards to. */
 int lowbit_pack(int fmt, const void* src, const uint16_t* src_scales,
                 int64_t n, int64_t k, void* codes, uint16_t* scales,
                 hipStream_t stream);
@@ -248,8 +259,9 @@ int lowbit_gemm_f32(int fmt, const void* codes, const uint16_t* scales,
  *            gate projection, f..2f-1 the up projection
  *   z_fp16 : [b][f] row-major FP16 (device, written)
  * SiLU(v) = v / (1 + e^-v) is evaluated in FP32 with the device expf; the
- * product is rounded once to FP16 (nearest-even; beyond the FP16 range it
- * becomes +-inf; a value that rounds to zero may come out as +0 or -0).
+ * FP32 product is rounded to FP16 (nearest-even; beyond the FP16 range it
+ * becomes +-inf; a zero keeps the IEEE sign of the product, e.g. -0 for
+ * v < -88 and u > 0, where e^-v overflows and SiLU(v) = -0).
  * f must be a multiple of 8. */
 int lowbit_silu_mul(const float* h_f32, int64_t f, int64_t b, uint16_t* z_fp16,
                     hipStream_t stream);

@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests (not a test module)."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -82,3 +84,23 @@ def full_weights(fmt, n, k, seed):
         hc, hs = oracle.t2_pack(ht, hsc)
         del ht
     return torch.from_numpy(hc).cuda(), dev_u16(hs), hc, hs
+
+
+def oracle_threads():
+    """Threads for oracle calls: the host's CPUs, at most 16 (ctypes releases
+    the GIL during each oracle call, so the calls run in parallel)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_blocks(call, total, axis, block=None):
+    """Concatenation along `axis` of call(start, count) over [0, total) in
+    blocks, computed on a thread pool.  `call` is an oracle function of a
+    row range; the blocks are independent, so the result equals one call
+    over the whole range."""
+    nt = oracle_threads()
+    if block is None:
+        block = max(1, -(-total // (4 * nt)))
+    starts = list(range(0, total, block))
+    with ThreadPoolExecutor(nt) as ex:
+        parts = list(ex.map(lambda s0: call(s0, min(block, total - s0)), starts))
+    return np.concatenate(parts, axis=axis)

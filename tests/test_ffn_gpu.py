@@ -68,16 +68,18 @@ def test_silu_mul_matches_oracle():
     h64 = h.astype(np.float64)
     z64 = np.array([[oracle.silu(v) for v in row] for row in h64[:, :f]]) * h64[:, f:]
     lo, hi = _fp16_bracket(z64)
-    # a value that rounds to zero may come out as either zero: SiLU(v)
-    # underflows in FP32 for v < -88, and the sign of a zero activation is
-    # not part of the contract (it only multiplies weights)
-    zero = ((lo & 0x7FFF) == 0) & ((z & 0x7FFF) == 0)
-    ok = (z == lo) | (z == hi) | zero
+    # zeros must carry the IEEE sign of the product: SiLU(-100) is -0 in FP32
+    # (e^100 overflows) and a tiny negative number in double; both round to
+    # the FP16 pattern 0x8000 once multiplied by 3
+    ok = (z == lo) | (z == hi)
     bad = np.argwhere(~ok)[:4].tolist()
     assert ok.all(), (f"{(~ok).sum()} values off, first at {bad}: got "
                       f"{[hex(z[i, j]) for i, j in bad]}, want {[hex(lo[i, j]) for i, j in bad]}")
     assert (lo != hi).sum() < 0.01 * z.size  # the allowance is rarely used
     assert z[0, 5] == 0x7C00  # SiLU(300) * 400 is beyond FP16: +inf
+    assert z[0, 2] == 0x8000  # SiLU(-100) * 3 = -0
+    assert z[0, 0] == 0x0000 and z[0, 1] == 0x0000  # SiLU(+0) * 1.5 = +0, SiLU(-0) * -2 = +0
+
 
 
 SMALL = [(128, 128, 1), (256, 384, 2), (384, 256, 3), (512, 640, 5), (1024, 512, 8),

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from bit_matmul_lowbit_amd import lowbit, synth
-from tests.helpers import TOL, assert_close, dev_u16, full_weights, host_u16, say
+from tests.helpers import TOL, assert_close, dev_u16, full_weights, host_u16, oracle_blocks, say
 
 pytestmark = pytest.mark.gpu
 
@@ -146,12 +146,11 @@ def test_full_pp512(fmt, m, n, k):
     yf, yb = yf.cpu().numpy(), host_u16(yb)
     assert np.array_equal(yb, _rne_f32_to_bf16(yf))
     f = oracle.Q1 if fmt == "q1" else oracle.T2
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 510, 511],
-                                     np.random.default_rng(2).integers(0, m, 24)]))
-    for r in rows:
-        ref = oracle.gemm(f, hc, hs, n, k, hx, m0=int(r), mrows=1)
-        assert_close(yf[r:r + 1], ref, f"gemm full {fmt} row {r}")
-        assert _bf16_ulp_ok(yb[r:r + 1], ref)
+    # every one of the 512 rows (the oracle runs on a thread pool)
+    ref = oracle_blocks(lambda m0, mr: oracle.gemm(f, hc, hs, n, k, hx, m0=m0, mrows=mr), m,
+                        axis=0, block=8)
+    assert_close(yf, ref, f"gemm full {fmt}")
+    assert _bf16_ulp_ok(yb, ref)
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])

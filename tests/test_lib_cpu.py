@@ -208,3 +208,24 @@ def test_ternary_storage_queries_and_validation(lib):
     assert lib.lowbit_t2_to_base3(good, good, 0, 128, good, good, st) == SHAPE
     assert lib.lowbit_base3_to_t2(good, good, 16, 128, bad_align, good, st) == ALIGN
     assert lib.lowbit_base3_to_t2(good, good, 16, 130, good, good, st) == SHAPE
+
+
+def test_binding_rejects_short_buffers(lib):
+    # the C interface takes no buffer lengths: the binding checks them on the
+    # host (plain CPU tensors stand in for device buffers here)
+    import torch
+
+    n, k = 40, 256
+    cb = lowbit.lowbit_codes_bytes("t2", n, k)
+    sb = lowbit.lowbit_scales_bytes("t2", n, k)
+    lowbit._need_planes("t2", n, k, torch.empty(cb, dtype=torch.uint8), torch.empty(sb // 2))
+    with pytest.raises(ValueError):
+        # Q1-sized codes passed as ternary would be read past their end
+        lowbit._need_planes("t2", n, k, torch.empty(lowbit.lowbit_codes_bytes("q1", n, k)),
+                            torch.empty(sb // 2))
+    with pytest.raises(ValueError):
+        lowbit._need_planes("q1", n, k, torch.empty(cb), torch.empty(sb // 2 - 1))
+    with pytest.raises(ValueError):
+        lowbit._need_numel(torch.empty(3, 7), 22, "out")
+    with pytest.raises(ValueError):
+        lowbit._need_shape(torch.empty(7, 3), (3, 7), "out")

@@ -209,6 +209,22 @@ def test_page_worked_example_seed42():
     assert codes.nbytes // 16 * 16 / 16 == 16  # 16 code bytes for this row tile
     assert 128 // 8 + 2 == 18
 
+    # The values the demonstration produces when run (the page shows the
+    # code, not its output): scale = max|w| = 0.2619945... in double, which
+    # is 0.261962890625 (pattern 0x3431) once the inputs are FP16; the first
+    # eight bits 0,0,0,1,0,0,1,0; 68 ones among the 128; reconstruction
+    # MSE 0.038976; 256 B of FP16 against 18 B, "14,2x".
+    assert scales[0] == 0x3431 and oracle.fp16_to_f64(scales[0]) == 0.261962890625
+    bits = [1 if d > 0 else 0 for d in dense]
+    assert bits[:8] == [0, 0, 0, 1, 0, 0, 1, 0]
+    assert sum(bits) == 68
+    # the oracle's scale is the FP16 rounding of the page's double scale
+    # (|ds| = 3.2e-5); MSE(s) = mean((|w| - s)^2) moves by at most
+    # 2 s |ds| = 1.7e-5 between the two scales
+    mse = sum((a - d) ** 2 for a, d in zip(vals, dense)) / 128
+    assert abs(mse - 0.038976) <= 2e-5, mse
+    assert round(256 / (128 // 8 + 2), 1) == 14.2
+
 
 # --------------------------------------------------------------------------
 # ternary pack / unpack  [P2]
