@@ -12,11 +12,21 @@ timed region.
 
 Printed: one JSON line with
   value      effective weight GB/s of whole steps (codes + scale bytes / time)
+  step_us_stats  min / median / p90 of the per-step time over chains of one
+             step per rotated copy (HIP events at the chain boundaries)
   roofline   weight-streaming kernel: algorithmic bytes per launch / its mean
-             duration from HIP events recorded on its launch stream, against
-             the 8 TB/s HBM peak; `traffic` is the HBM bytes per launch that
+             duration from HIP events recorded on its launch stream (>= 10
+             back-to-back chains; min / median / p90 in kernel_us_stats),
+             against the 8 TB/s HBM peak and against the measured
+             streaming-read ceiling; `traffic` is the HBM bytes per launch that
              rocprofv3 counters gave for the same kernel source, or null
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+  ceilings   measured on this GPU: a streaming read of 4 GiB (best of a sweep
+             of launch shapes), LDS read bandwidth, and a BF16 matrix-core
+             loop (include/lowbit_probes.h)
+  provenance seeds, SHA-256 of the inputs, library and device versions
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
+             on all host threads (at most 16) and on one; plus oracle GEMM
+             GFLOPS and the CPU FP16 -> Q1 quantisation time
   secondary  the other workloads: decode GEMVs (fused FFN shapes, batch
              sweep), the decode FFN chain (gate+up GEMV, SiLU-gated
              product, down GEMV; eager and as a graph), the two ends of
@@ -26,10 +36,12 @@ Printed: one JSON line with
              quantiser and the pp512 prefill GEMMs;
              for the GEMVs also the per-step time of a HIP graph that holds
              one step per rotated copy (small matrices are otherwise timed
-             by the host's launch rate); the GEMMs' `us` is the device time
-             per GEMM of a replayed graph of 50 launches (`eager_us`: the
-             same launches issued from Python, whose per-call cost is about
-             one GEMM)
+             by the host's launch rate); the GEMMs' `us` is the median device
+             time per GEMM of a replayed graph with one launch per rotated
+             set of codes, scales, X and Y (>= 1 GiB: cold), `hot_us` the
+             same for 50 launches on one set (cache-resident), and
+             `dense_bf16_torch_matmul` a library GEMM on dense BF16 operands
+             of the same shape (context)
 ``--gpus N`` with N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -96,10 +108,46 @@ def rotated_copies(codes, scales):
     return [(codes.clone(), scales.clone()) for _ in range(r)], nbytes
 
 
+def sha256_dev(t):
+    """SHA-256 (hex prefix) of a device tensor's bytes."""
+    import torch
+
+    return hashlib.sha256(t.contiguous().view(torch.uint8).cpu().numpy().tobytes()).hexdigest()[:16]
+
+
+def provenance(sha, seeds):
+    import numpy as np
+    import torch
+
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"seeds": seeds, "input_sha256": sha, "numpy": np.__version__, "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None), "rocm": rocm,
+            "device": torch.cuda.get_device_name(0)}
+
+
+def stats(xs):
+    """min / median / p90 / mean of a list of numbers (rounded for the JSON)."""
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64)
+    return {"n": int(a.size), "min": float(a.min()), "median": float(np.median(a)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
+
+
+def rounded(d, nd=3):
+    return {k: (round(v, nd) if isinstance(v, float) else v) for k, v in d.items()}
+
+
 # ---------------------------------------------------------------------------
 # GEMV timing
 
-def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_graph=False):
+def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_graph=False,
+              with_hash=False):
     """Returns dict with step GB/s, ms/step and the mean accumulate-kernel time;
     with_graph adds the per-step time of a HIP graph holding one step per
     rotated copy (prepare + accumulate, no host work between launches)."""
@@ -108,9 +156,11 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
     from bit_matmul_lowbit_amd import lowbit, synth
 
     codes, scales = make_weights(fmt, n, k, seed)
+    x = synth.dev_fp16_normal((b, k), 1.0, seed + 2)
+    sha = {"codes": sha256_dev(codes), "scales": sha256_dev(scales), "x": sha256_dev(x)} \
+        if with_hash else None
     copies, wbytes = rotated_copies(codes, scales)
     del codes, scales
-    x = synth.dev_fp16_normal((b, k), 1.0, seed + 2)
     y = torch.empty((b, n), dtype=torch.float32, device="cuda")
     ws = torch.empty(lowbit.lowbit_gemv_workspace_bytes(fmt, n, k, b), dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream()
@@ -128,27 +178,43 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
         step(i)
     torch.cuda.synchronize()
 
-    # whole steps, wall clock bracketed by device synchronisation
+    # whole steps, wall clock bracketed by device synchronisation; HIP events
+    # on the launch stream at every chain boundary (one chain = one step per
+    # rotated copy) give the spread of the per-step time over the chains
+    nc = len(copies)
+    marks = []
     t0 = time.perf_counter()
     for i in range(steps):
+        if i % nc == 0:
+            marks.append((i, torch.cuda.Event(enable_timing=True)))
+            marks[-1][1].record(st)
         step(warmup + i)
+    marks.append((steps, torch.cuda.Event(enable_timing=True)))
+    marks[-1][1].record(st)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    chain_step_ms = [a[1].elapsed_time(b_[1]) / (b_[0] - a[0]) for a, b_ in zip(marks, marks[1:])
+                     if b_[0] - a[0] == nc]
 
-    kernel_ms = None
+    kernel_ms = kernel_stats = None
     if with_kernel_events:
-        # the weight-streaming kernel alone: a back-to-back chain of
-        # accumulate launches (one per rotated copy) between two HIP events
-        # recorded on the launch stream, so dispatch gaps are amortised
+        # the weight-streaming kernel alone: back-to-back chains of
+        # accumulate launches (one per rotated copy), each chain between two
+        # HIP events recorded on the launch stream so that dispatch gaps are
+        # amortised; at least 10 chains and as many launches as timed steps
         lowbit.lowbit_gemv_prepare(n, k, x, y, ws, stream=st)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(st)
-        for i in range(steps):
-            c, s = copies[i % len(copies)]
-            lowbit.lowbit_gemv_accumulate(fmt, c, s, n, k, b, y, ws, stream=st)
-        ev1.record(st)
+        nchains = max(10, -(-steps // nc))
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nchains + 1)]
+        evs[0].record(st)
+        for j in range(nchains):
+            for i in range(nc):
+                c, s = copies[i]
+                lowbit.lowbit_gemv_accumulate(fmt, c, s, n, k, b, y, ws, stream=st)
+            evs[j + 1].record(st)
         torch.cuda.synchronize()
-        kernel_ms = ev0.elapsed_time(ev1) / steps
+        per = [evs[j].elapsed_time(evs[j + 1]) / nc for j in range(nchains)]
+        kernel_ms = sum(per) / len(per)
+        kernel_stats = stats([v * 1e3 for v in per])
 
     graph_ms = None
     if with_graph:
@@ -181,7 +247,10 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
         "ms_per_step": elapsed / steps * 1e3,
         "gbs": wbytes * steps / elapsed / 1e9,
         "kernel_ms": kernel_ms,
+        "kernel_us_stats": kernel_stats,
+        "step_us_stats": stats([v * 1e3 for v in chain_step_ms]) if chain_step_ms else None,
         "graph_ms_per_step": graph_ms,
+        "sha256": sha,
     }
     del copies
     torch.cuda.empty_cache()
@@ -360,6 +429,11 @@ def time_quantize(n, k, seed, steps, warmup):
 
 
 def time_gemm(fmt, m, n, k, seed, steps, warmup):
+    """pp512 GEMM: per-GEMM device time of a replayed HIP graph of launches,
+    (a) cold: one launch per distinct set of (codes, scales, X, Y), the sets
+    totalling >= 1 GiB, so weights and activations come from HBM as for
+    successive layers; (b) hot: `steps` launches on one set (cache-resident,
+    context).  Each graph is replayed 10 times: min / median / p90 per GEMM."""
     import torch
 
     from bit_matmul_lowbit_amd import lowbit, synth
@@ -367,6 +441,9 @@ def time_gemm(fmt, m, n, k, seed, steps, warmup):
     codes, scales = make_weights(fmt, n, k, seed)
     x = synth.dev_bf16_normal((m, k), 1.0, seed + 2)
     y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    set_bytes = codes.numel() + scales.numel() * 2 + x.numel() * 2 + y.numel() * 2
+    r = max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    sets = [(codes.clone(), scales.clone(), x.clone(), torch.empty_like(y)) for _ in range(r)]
     for _ in range(warmup):
         lowbit.lowbit_gemm(fmt, codes, scales, n, k, x, out=y)
     torch.cuda.synchronize()
@@ -377,40 +454,202 @@ def time_gemm(fmt, m, n, k, seed, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     eager_ms = a.elapsed_time(b) / steps
-    # The same launches captured once in a HIP graph and replayed: the device
-    # time of back-to-back GEMMs without the Python binding's per-call cost
-    # (which is about as long as one GEMM).  The kernel writes y and touches no
-    # other memory, so replays are independent.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            for _ in range(steps):
-                lowbit.lowbit_gemm(fmt, codes, scales, n, k, x, out=y, stream=side)
-    torch.cuda.current_stream().wait_stream(side)
-    g.replay()
-    torch.cuda.synchronize()
-    best = None
-    for _ in range(3):
-        a.record()
+
+    def graph_stats(launch_list):
+        # the launches captured once and replayed; the kernel writes only its
+        # Y, so replays are independent
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for c, sc, xx, yy in launch_list:
+                    lowbit.lowbit_gemm(fmt, c, sc, n, k, xx, out=yy, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
         g.replay()
-        b.record()
         torch.cuda.synchronize()
-        t = a.elapsed_time(b) / steps
-        best = t if best is None else min(best, t)
-    del g
-    ms = best
+        ts = []
+        for _ in range(10):
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / len(launch_list) * 1e3)
+        del g
+        return stats(ts)
+
+    cold = graph_stats(sets)
+    hot = graph_stats([(codes, scales, x, y)] * steps)
+    del sets
+    torch.cuda.empty_cache()
     flops = 2.0 * m * n * k
-    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-            "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "eager_ms": eager_ms}
+    us = cold["median"]
+    return {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
+            "frac_bf16_peak": flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "cold_us": rounded(cold, 2), "rotated_sets": r,
+            "hot_us": rounded(hot, 2),
+            "hot_tflops": round(flops / (hot["median"] * 1e-6) / 1e12, 1),
+            "eager_us": eager_ms * 1e3}
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, single-threaded, on a bounded sample
+# measured ceilings (context for the roofline): a streaming read over 4 GiB
+# and a matrix-core loop, each doing nothing but the one thing it measures
 
-def cpu_baseline(fmt, n, k, seed, budget_s=12.0):
+def ceilings():
+    import numpy as np
+    import torch
+
+    from bit_matmul_lowbit_amd import lowbit
+
+    cus = lowbit.lowbit_probe_cu_count()
+    out = {"compute_units": cus}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)  # touch every page before timing
+    sink = torch.zeros(64 * cus, dtype=torch.int32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def read_gbs(bpc, order, reps):
+        lowbit.lowbit_probe_stream_read(buf, bpc, sink, order)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a.record()
+            lowbit.lowbit_probe_stream_read(buf, bpc, sink, order)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return [nbytes / (t * 1e-3) / 1e9 for t in ts]
+
+    # launch shapes: work-groups per CU x (0: grid-stride, 1: a contiguous
+    # share per work-group); the best is timed 10 more times
+    sweep = {(bpc, order): max(read_gbs(bpc, order, 3))
+             for order in (0, 1) for bpc in (1, 2, 4, 8, 16, 32)}
+    best = max(sweep, key=sweep.get)
+    rates = read_gbs(best[0], best[1], 10)
+    out["stream_read"] = {"bytes": nbytes, "blocks_per_cu": best[0],
+                          "order": "grid-stride" if best[1] == 0 else "contiguous share per work-group",
+                          "gbs": rounded(stats(rates), 1),
+                          "sweep_gbs": {f"{k[0]}/cu,{'stride' if k[1] == 0 else 'share'}": round(v, 1)
+                                        for k, v in sweep.items()},
+                          "frac_of_hbm_peak": round(float(np.median(rates)) / HBM_PEAK_GBS, 4)}
+    del buf, sink
+    torch.cuda.empty_cache()
+
+    lsink = torch.zeros(4 * cus * 256, dtype=torch.int32, device="cuda")
+    lres = {}
+    for bpc in (1, 2, 4):
+        lowbit.lowbit_probe_lds_read(100, bpc, lsink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a.record()
+            nb = lowbit.lowbit_probe_lds_read(4000, bpc, lsink)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(nb / (a.elapsed_time(b) * 1e-3))
+        lres[bpc] = ts
+    best = max(lres, key=lambda k: float(np.median(lres[k])))
+    med = float(np.median(lres[best]))
+    out["lds_read"] = {"blocks_per_cu": best, "tb_per_s": round(med / 1e12, 2),
+                       "bytes_per_clk_per_cu_at_2p4ghz": round(med / cus / 2.4e9, 1),
+                       "sweep_tb_per_s": {str(k): round(float(np.median(v)) / 1e12, 2)
+                                          for k, v in lres.items()}}
+    del lsink
+
+    msink = torch.zeros(8 * cus * 256, dtype=torch.float32, device="cuda")
+    iters = 20000
+    res = {}
+    for bpc in (1, 2):
+        lowbit.lowbit_probe_mfma_bf16(100, bpc, msink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a.record()
+            flops = lowbit.lowbit_probe_mfma_bf16(iters, bpc, msink)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        res[bpc] = [flops / (t * 1e-3) / 1e12 for t in ts]
+    best = max(res, key=lambda k: max(res[k]))
+    out["mfma_bf16_32x32x16"] = {"blocks_per_cu": best, "waves_per_simd": best,
+                                 "tflops": rounded(stats(res[best]), 1),
+                                 "frac_of_bf16_peak": round(float(sorted(res[best])[2]) / BF16_PEAK_TFLOPS, 4)}
+    del msink
+    torch.cuda.empty_cache()
+    return out
+
+
+def dense_gemm_context(m, n, k, seed, reps=50):
+    """torch.matmul (hipBLASLt) on dense BF16 operands of the same pp512
+    shape: what a tuned library reaches at M = 512 on this GPU (context)."""
+    import torch
+
+    from bit_matmul_lowbit_amd import synth
+
+    x = synth.dev_bf16_normal((m, k), 1.0, seed)
+    w_nk = synth.dev_bf16_normal((n, k), 0.1, seed + 1)  # W as stored: [n][k]
+    w_kn = w_nk.t().contiguous()
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name, wt in (("x_wT", w_nk.t()), ("x_w", w_kn)):
+        for _ in range(10):
+            torch.matmul(x, wt, out=y)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a.record()
+            for _ in range(reps):
+                torch.matmul(x, wt, out=y)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / reps)
+        ms = min(ts)
+        out[name] = {"us": round(ms * 1e3, 2), "tflops": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1)}
+    del x, w_nk, w_kn, y
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample, on one thread
+# and on all host threads (ctypes releases the GIL during each oracle call)
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rows_rate(call, total_rows, threads, budget_s, chunk):
+    """Run call(r0, r) over successive row ranges of `chunk` rows (wrapping
+    at total_rows) on `threads` threads until about budget_s of wall time
+    has passed; returns (rows done, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    done = 0
+    t0 = time.perf_counter()
+    nxt = 0
+    with ThreadPoolExecutor(threads) as ex:
+        while time.perf_counter() - t0 < budget_s:
+            starts = []
+            for _ in range(threads):
+                r0 = nxt % total_rows
+                r = min(chunk, total_rows - r0)
+                starts.append((r0, r))
+                nxt += r
+            list(ex.map(lambda a: call(*a), starts))
+            done += sum(r for _, r in starts)
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(fmt, n, k, seed, budget_s=6.0):
     import numpy as np
     import torch
 
@@ -423,24 +662,62 @@ def cpu_baseline(fmt, n, k, seed, budget_s=12.0):
     hc = codes.cpu().numpy()
     hs = scales.view(torch.int16).cpu().numpy().view(np.uint16)
     hx = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    del codes, scales
     f = oracle.Q1 if fmt == "q1" else oracle.T2
     per_row = (lowbit_codes_bytes(fmt, n, k) + lowbit_scales_bytes(fmt, n, k)) / ((n + 15) // 16 * 16)
-    # whole passes over the matrix (2048-row chunks) until about budget_s of
-    # CPU time has been spent
-    rows_done, t_used, chunk, passes = 0, 0.0, 2048, 0
-    while t_used < budget_s:
-        r0 = rows_done % n
-        r = min(chunk, n - r0)
-        t0 = time.perf_counter()
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def gemv_rows(r0, r):
         oracle.gemv(f, hc, hs, n, k, hx, row0=r0, nrows=r)
-        t_used += time.perf_counter() - t0
-        rows_done += r
-    passes = rows_done / n
-    gbs = rows_done * per_row / t_used / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle GEMV (scalar C, double precision, 1 thread) over {passes:.2f} passes of "
-                      f"the same {fmt} {n}x{k} matrix and x, b=1 ({rows_done} rows, {t_used:.1f} s of "
-                      f"CPU time); host has {os.cpu_count()} logical CPUs"}
+
+    rows1, t1 = _oracle_rows_rate(gemv_rows, n, 1, budget_s, 2048)
+    rowsn, tn = _oracle_rows_rate(gemv_rows, n, threads, budget_s, 2048)
+    gbs1 = rows1 * per_row / t1 / 1e9
+    gbsn = rowsn * per_row / tn / 1e9
+
+    # oracle GEMM (one X row per call) on the ternary pp512 shape, and the
+    # CPU Q1 quantiser on rows of the quantiser workload, all threads
+    gm, gn, gk = 512, 6144, 2048
+    gc, gs = make_weights("t2", gn, gk, 1004 + gn)
+    gx = synth.dev_bf16_normal((gm, gk), 1.0, 1004 + gn + 2)
+    hgc = gc.cpu().numpy()
+    hgs = gs.view(torch.int16).cpu().numpy().view(np.uint16)
+    hgx = gx.view(torch.int16).cpu().numpy().view(np.uint16)
+    del gc, gs, gx
+
+    def gemm_rows(m0, mr):
+        oracle.gemm(oracle.T2, hgc, hgs, gn, gk, hgx, m0=m0, mrows=mr)
+
+    mrows, tg = _oracle_rows_rate(gemm_rows, gm, threads, budget_s / 2, 1)
+    gemm_gflops = 2.0 * mrows * gn * gk / tg / 1e9
+
+    # the whole FP16 -> Q1 quantisation of the 151936 x 5120 matrix, in
+    # 1024-row blocks on all threads
+    qn, qk = 151936, 5120
+    w = synth.dev_fp16_normal((qn, qk), 0.02, 1003)
+    hw = w.view(torch.int16).cpu().numpy().view(np.uint16)
+    del w
+    blocks = [hw[i:i + 1024] for i in range(0, qn, 1024)]
+    from concurrent.futures import ThreadPoolExecutor
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda blk: oracle.q1_quantize(np.ascontiguousarray(blk)), blocks))
+    q_full_s = time.perf_counter() - t0
+    del hw, blocks
+
+    return {"value": round(gbsn, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle GEMV (scalar C, double precision) over row ranges of the same {fmt} "
+                      f"{n}x{k} matrix and x, b=1, on {threads} threads ({rowsn} rows in {tn:.1f} s); "
+                      f"host: {os.cpu_count()} logical CPUs, {cpu_model()}",
+            "single_thread": {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{rows1} rows in {t1:.1f} s"},
+            "gemm_pp512_t2_gflops": {"value": round(gemm_gflops, 3), "cores": threads,
+                                     "sample": f"{mrows} X rows (the 512 rows of the 512x6144x2048 "
+                                               f"ternary GEMM, repeated) in {tg:.1f} s"},
+            "q1_quantize_151936x5120_s": {"value": round(q_full_s, 2), "cores": threads,
+                                          "sample": "the whole 151936x5120 FP16 matrix"},
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}
 
 
 # ---------------------------------------------------------------------------
@@ -472,6 +749,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="t2_lmhead_152k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming-read and matrix-core ceiling probes")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary", default="all",
                     help="comma-separated secondary groups to run: gemv, quantize, ffn, "
@@ -500,7 +779,7 @@ def main():
 
     fmt, n, k, b, seed = WORKLOADS[args.workload]
     log(f"[bench] {args.workload}: {fmt} {n}x{k} b={b}, {args.steps} steps, {args.warmup} warmup")
-    r = time_gemv(fmt, n, k, b, seed, args.steps, args.warmup)
+    r = time_gemv(fmt, n, k, b, seed, args.steps, args.warmup, with_hash=True)
     achieved = r["weight_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
     log(f"[bench] step {r['ms_per_step'] * 1e3:.2f} us, {r['gbs']:.1f} GB/s; "
         f"accumulate kernel {r['kernel_ms'] * 1e3:.2f} us, {achieved:.1f} GB/s")
@@ -546,8 +825,19 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_record(kernel_src),
             "kernel_us": round(r["kernel_ms"] * 1e3, 3),
+            "kernel_us_stats": rounded(r["kernel_us_stats"], 3),
         },
+        "step_us_stats": rounded(r["step_us_stats"], 3) if r["step_us_stats"] else None,
+        "provenance": provenance(r["sha256"], {"weights": seed, "x": seed + 2}),
     }
+
+    if not args.no_ceilings:
+        log("[bench] ceiling probes ...")
+        ceil = ceilings()
+        result["ceilings"] = ceil
+        med = ceil["stream_read"]["gbs"]["median"]
+        result["roofline"]["frac_of_measured_stream_read"] = round(achieved / med, 4)
+        log(f"[bench] ceilings: {ceil}")
 
     if not args.no_secondary:
         sec = {}
@@ -563,6 +853,7 @@ def main():
                 rr = time_gemv(f2, n2, k2, b2, seeds, 50, 10, with_graph=True)
                 sec[key] = {"gbs": round(rr["gbs"], 1), "us_per_step": round(rr["ms_per_step"] * 1e3, 2),
                             "kernel_gbs": round(rr["weight_bytes"] / (rr["kernel_ms"] * 1e-3) / 1e9, 1),
+                            "kernel_us": rounded(rr["kernel_us_stats"], 2),
                             "graph_us_per_step": round(rr["graph_ms_per_step"] * 1e3, 2),
                             "graph_gbs": round(rr["weight_bytes"] / (rr["graph_ms_per_step"] * 1e-3) / 1e9, 1)}
                 log(f"[bench] {key}: {sec[key]}")
@@ -587,9 +878,14 @@ def main():
                                        "gemm_pp512_q1_512x2048x6144": ("q1", 512, 2048, 6144)}.items() \
                 if "gemm" in chosen else ():
             g = time_gemm(f2, m2, n2, k2, 1004 + n2, 50, 10)
-            sec[key] = {"tflops": round(g["tflops"], 2), "us": round(g["ms"] * 1e3, 2),
+            sec[key] = {"tflops": round(g["tflops"], 2), "us": round(g["us"], 2),
                         "frac_bf16_peak": round(g["frac_bf16_peak"], 4),
-                        "eager_us": round(g["eager_ms"] * 1e3, 2)}
+                        "timing": "cold: median over 10 replays of a graph with one GEMM per "
+                                  f"rotated set of codes, scales, X and Y ({g['rotated_sets']} sets "
+                                  ">= 1 GiB)",
+                        "cold_us": g["cold_us"], "hot_us": g["hot_us"], "hot_tflops": g["hot_tflops"],
+                        "eager_us": round(g["eager_us"], 2),
+                        "dense_bf16_torch_matmul": dense_gemm_context(m2, n2, k2, 77 + n2)}
             log(f"[bench] {key}: {sec[key]}")
         result["secondary"] = sec
 

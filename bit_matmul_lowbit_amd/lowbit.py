@@ -31,6 +31,11 @@ SYMBOLS = [
 ]
 
 
+# ceiling probes (include/lowbit_probes.h): context for the roofline only
+PROBE_SYMBOLS = ["lowbit_probe_stream_read", "lowbit_probe_mfma_bf16", "lowbit_probe_lds_read",
+                 "lowbit_probe_cu_count"]
+
+
 class LowbitError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -78,6 +83,10 @@ def load() -> ctypes.CDLL:
         "lowbit_base3_bytes": ([i64, i64], sz),
         "lowbit_t2_to_base3": ([p, p, i64, i64, p, p, p], i),
         "lowbit_base3_to_t2": ([p, p, i64, i64, p, p, p], i),
+        "lowbit_probe_stream_read": ([p, sz, i, i, p, p], i),
+        "lowbit_probe_mfma_bf16": ([i, i, p, p], i),
+        "lowbit_probe_lds_read": ([i, i, p, p], i),
+        "lowbit_probe_cu_count": ([], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -495,3 +504,45 @@ def lowbit_base3_to_t2(b3, scales_rm, n: int, k: int, codes=None, scales=None, s
                                      _dev(scales, (torch.float16, torch.int16), "scales"),
                                      _stream(stream)), "lowbit_base3_to_t2")
     return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# ceiling probes (context for the roofline, not part of the path)
+
+def lowbit_probe_cu_count() -> int:
+    return int(load().lowbit_probe_cu_count())
+
+
+def lowbit_probe_stream_read(buf, blocks_per_cu: int, sink, order: int = 0, stream=None):
+    """Read every byte of the device tensor `buf` once (streaming-read probe;
+    order 0 grid-stride, 1 one contiguous share per work-group)."""
+    import torch
+
+    nbytes = buf.numel() * buf.element_size()
+    _need_numel(sink, blocks_per_cu * lowbit_probe_cu_count(), "sink")
+    _check(load().lowbit_probe_stream_read(_dev(buf, (buf.dtype,), "buf"), nbytes, blocks_per_cu,
+                                           order, _dev(sink, (torch.int32, torch.uint32), "sink"),
+                                           _stream(stream)), "lowbit_probe_stream_read")
+
+
+def lowbit_probe_mfma_bf16(iters: int, blocks_per_cu: int, sink, stream=None):
+    """Matrix-core loop probe; returns the flops it executes."""
+    import torch
+
+    blocks = blocks_per_cu * lowbit_probe_cu_count()
+    _need_numel(sink, blocks * 256, "sink")
+    _check(load().lowbit_probe_mfma_bf16(iters, blocks_per_cu, _dev(sink, (torch.float32,), "sink"),
+                                         _stream(stream)), "lowbit_probe_mfma_bf16")
+    return blocks * 4 * iters * 4 * 2 * 32 * 32 * 16
+
+
+def lowbit_probe_lds_read(iters: int, blocks_per_cu: int, sink, stream=None):
+    """LDS read-bandwidth probe; returns the bytes it reads from LDS."""
+    import torch
+
+    blocks = blocks_per_cu * lowbit_probe_cu_count()
+    _need_numel(sink, blocks * 256, "sink")
+    _check(load().lowbit_probe_lds_read(iters, blocks_per_cu,
+                                        _dev(sink, (torch.int32, torch.uint32), "sink"),
+                                        _stream(stream)), "lowbit_probe_lds_read")
+    return blocks * 256 * iters * 8 * 16

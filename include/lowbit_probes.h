@@ -1,0 +1,63 @@
+/*
+ * lowbit_probes.h -- measured ceilings for the roofline of liblowbit.so's
+ * kernels on this GPU.  Context only: neither probe is part of the y = W.x
+ * path; bench.py times them next to the kernels, so that a kernel's rate can
+ * be set against what the machine delivers to a kernel that does nothing
+ * else, as well as against the vendor's peak figures.
+ *
+ * [P2] 7minutos.es, "PrismML lanza Bonsai 27B ...", "Rendimiento y
+ * decodificacion especulativa DSpark": decode is bound by memory bandwidth,
+ * prefill by compute -- hence one probe of each.
+ *
+ * Conventions as in lowbit.h: device pointers, host-side validation, the
+ * kernels are enqueued on `stream` and the call returns without waiting.
+ */
+#ifndef LOWBIT_PROBES_H
+#define LOWBIT_PROBES_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Streaming read of `bytes` bytes of device memory at `buf` (16-byte
+ * aligned, bytes a multiple of 16, at most 2^40): a grid of
+ * blocks_per_cu * (compute units) work-groups of 256 threads, each thread
+ * keeping 8 independent 16-byte loads in flight.  order 0: the whole grid
+ * reads one contiguous stretch per step (grid-stride order); order 1: each
+ * work-group sweeps its own contiguous share.  The data are folded with
+ * XOR; `sink` ([blocks] uint32, device) is written only if a fold equals a
+ * fixed 32-bit constant, so the call writes (next to) nothing.
+ * 1 <= blocks_per_cu <= 64.  Returns a lowbit_status. */
+int lowbit_probe_stream_read(const void* buf, size_t bytes, int blocks_per_cu, int order,
+                             uint32_t* sink, hipStream_t stream);
+
+/* Matrix-core loop: every wave of blocks_per_cu * (compute units)
+ * work-groups of 256 threads issues `iters` x 4 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands (2 * 32 * 32 * 16 flop
+ * each) and nothing else; `sink` ([blocks * 256] float, device) is written
+ * only if a result equals a fixed constant.  1 <= blocks_per_cu <= 8,
+ * 1 <= iters <= 2^24.  Returns a lowbit_status. */
+int lowbit_probe_mfma_bf16(int iters, int blocks_per_cu, float* sink, hipStream_t stream);
+
+/* LDS read bandwidth: blocks_per_cu * (compute units) work-groups of 256
+ * threads; each thread fills its 16-byte slots of a 32 KB LDS buffer, then
+ * reads `iters` x 8 of them with 128-bit LDS loads (consecutive lanes on
+ * consecutive 16-byte slots: no bank conflicts), folding them with XOR;
+ * `sink` ([blocks * 256] uint32, device) is written only if a fold equals
+ * a fixed constant.  Bytes read = blocks * 256 * iters * 8 * 16.
+ * 1 <= blocks_per_cu <= 4, 1 <= iters <= 2^24.  Returns a lowbit_status. */
+int lowbit_probe_lds_read(int iters, int blocks_per_cu, uint32_t* sink, hipStream_t stream);
+
+/* Compute units of the current device, as the probes and the kernels'
+ * launchers count them (256 if the query fails). */
+int lowbit_probe_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_PROBES_H */

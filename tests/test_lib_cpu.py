@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert lib.lowbit_version() == 1
     for s in range(7):
-        assert lowbit.status_str(s)
+        assert lowbit.status_str(s) != "unknown status"
     assert lowbit.status_str(99) == "unknown status"
 
 
@@ -229,3 +229,22 @@ def test_binding_rejects_short_buffers(lib):
         lowbit._need_numel(torch.empty(3, 7), 22, "out")
     with pytest.raises(ValueError):
         lowbit._need_shape(torch.empty(7, 3), (3, 7), "out")
+
+
+def test_probe_header_and_exports(lib):
+    text = open(os.path.join(ROOT, "include", "lowbit_probes.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(lowbit_probe_\w+)\s*\(", text, flags=re.M)
+    assert names == lowbit.PROBE_SYMBOLS
+    for name in names:
+        assert hasattr(lib, name), name
+    good = ctypes.c_void_p(1 << 20)
+    st = ctypes.c_void_p(0)
+    assert lib.lowbit_probe_stream_read(good, 100, 4, 0, good, st) == SHAPE
+    assert lib.lowbit_probe_stream_read(good, 1 << 20, 0, 0, good, st) == ARG
+    assert lib.lowbit_probe_stream_read(good, 1 << 20, 4, 2, good, st) == ARG
+    assert lib.lowbit_probe_stream_read(ctypes.c_void_p(8), 1 << 20, 4, 1, good, st) == ALIGN
+    assert lib.lowbit_probe_mfma_bf16(0, 2, good, st) == ARG
+    assert lib.lowbit_probe_mfma_bf16(100, 9, good, st) == ARG
+    assert lib.lowbit_probe_lds_read(100, 5, good, st) == ARG
+    assert lib.lowbit_probe_lds_read(0, 2, good, st) == ARG
