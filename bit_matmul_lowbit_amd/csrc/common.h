@@ -127,6 +127,12 @@ hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint
 hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t* scales,
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st);
+// lowbit_gemv with its scratch in a static device array (no workspace):
+// at most gemv_noalloc_scratch_bytes() of scratch, checked by the caller
+size_t gemv_noalloc_scratch_bytes();
+hipError_t launch_gemv_noalloc(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                               int64_t k, const uint16_t* x, int64_t b, float* y,
+                               hipStream_t st);
 
 // decode FFN: SiLU(gate) * up -> FP16, and the whole gated-MLP chain
 hipError_t launch_silu_mul(const float* h, int64_t f, int64_t b, uint16_t* z, hipStream_t st);

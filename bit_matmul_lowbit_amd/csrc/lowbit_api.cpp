@@ -60,6 +60,7 @@ const char* lowbit_status_str(int status) {
     case LOWBIT_ERR_UNSUPPORTED: return "unsupported request";
     case LOWBIT_ERR_HIP: return "HIP launch failed";
     case LOWBIT_ERR_WORKSPACE: return "workspace missing or too small";
+    case LOWBIT_ERR_SCRATCH: return "request needs more than the static scratch (1 MiB)";
     default: return "unknown status";
   }
 }
@@ -159,6 +160,20 @@ int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales, int64_t n, i
   if (st != LOWBIT_OK) return st;
   return lowbit_gemv_accumulate(fmt, codes, scales, n, k, b, y_f32, workspace, workspace_bytes,
                                 stream);
+}
+
+int lowbit_gemv_noalloc(int fmt, const void* codes, const uint16_t* scales, int64_t n,
+                        int64_t k, const uint16_t* x_fp16, int64_t b, float* y_f32,
+                        hipStream_t stream) {
+  if (!fmt_ok(fmt) || !codes || !scales || !x_fp16 || !y_f32) return LOWBIT_ERR_ARG;
+  if (b < 1 || b > 8) return LOWBIT_ERR_ARG;
+  if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_fp16) || !aligned16(y_f32))
+    return LOWBIT_ERR_ALIGN;
+  if (lowbit::gemv_workspace_bytes(k, b) > lowbit::gemv_noalloc_scratch_bytes())
+    return LOWBIT_ERR_SCRATCH;
+  return hip_status(lowbit::launch_gemv_noalloc(fmt, static_cast<const uint8_t*>(codes), scales,
+                                                n, k, x_fp16, b, y_f32, stream));
 }
 
 static int gemm_common(int fmt, const void* codes, const uint16_t* scales, int64_t n, int64_t k,

@@ -25,7 +25,7 @@ SYMBOLS = [
     "lowbit_quantize_q1", "lowbit_pack_t2", "lowbit_pack", "lowbit_unpack",
     "lowbit_quantize_t2", "lowbit_base3_bytes", "lowbit_t2_to_base3", "lowbit_base3_to_t2",
     "lowbit_gemv_workspace_bytes", "lowbit_gemv_prepare", "lowbit_gemv_accumulate",
-    "lowbit_gemv", "lowbit_gemm", "lowbit_gemm_f32", "lowbit_silu_mul",
+    "lowbit_gemv", "lowbit_gemv_noalloc", "lowbit_gemm", "lowbit_gemm_f32", "lowbit_silu_mul",
     "lowbit_ffn_workspace_bytes", "lowbit_ffn", "lowbit_embed", "lowbit_argmax_workspace_bytes",
     "lowbit_argmax", "lowbit_lm_head_workspace_bytes", "lowbit_lm_head",
 ]
@@ -69,6 +69,7 @@ def load() -> ctypes.CDLL:
         "lowbit_gemv_prepare": ([i64, i64, p, i64, p, p, sz, p], i),
         "lowbit_gemv_accumulate": ([i, p, p, i64, i64, i64, p, p, sz, p], i),
         "lowbit_gemv": ([i, p, p, i64, i64, p, i64, p, p, sz, p], i),
+        "lowbit_gemv_noalloc": ([i, p, p, i64, i64, p, i64, p, p], i),
         "lowbit_gemm": ([i, p, p, i64, i64, p, i64, p, p], i),
         "lowbit_gemm_f32": ([i, p, p, i64, i64, p, i64, p, p], i),
         "lowbit_silu_mul": ([p, i64, i64, p, p], i),
@@ -259,6 +260,28 @@ def lowbit_gemv(fmt, codes, scales, n: int, k: int, x, out=None, workspace=None,
                               _dev(out, (torch.float32,), "out"),
                               _dev(workspace, (torch.uint8,), "workspace"),
                               workspace.numel(), _stream(stream)), "lowbit_gemv")
+    return out
+
+
+def lowbit_gemv_noalloc(fmt, codes, scales, n: int, k: int, x, out=None, stream=None):
+    """x FP16 [b][k] (or [k]) -> y FP32 [b][n], with the library's static
+    scratch instead of a workspace (the library allocates nothing; pass
+    `out` to allocate nothing here either)."""
+    import torch
+
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    b = x2.shape[0]
+    if x2.shape[1] != k:
+        raise ValueError("x must have k columns")
+    _need_planes(fmt, n, k, codes, scales)
+    if out is None:
+        out = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _need_numel(out, b * n, "out")
+    _check(load().lowbit_gemv_noalloc(_fmt(fmt), _dev(codes, (torch.uint8,), "codes"),
+                                      _dev(scales, (torch.float16, torch.int16), "scales"), n, k,
+                                      _dev(x2, (torch.float16,), "x"), b,
+                                      _dev(out, (torch.float32,), "out"), _stream(stream)),
+           "lowbit_gemv_noalloc")
     return out
 
 

@@ -62,9 +62,11 @@
  *
  *   - Pointers are HIP device pointers unless stated otherwise; the caller
  *     allocates and frees every buffer.  The library never allocates,
- *     frees or synchronises, and keeps no state between calls.
+ *     frees or synchronises, and keeps no state between calls (apart from
+ *     lowbit_gemv_noalloc's static scratch, below).
  *   - Outputs that kernels accumulate with FP32 atomic adds -- y of
- *     lowbit_gemv, lowbit_gemv_accumulate, lowbit_ffn and lowbit_lm_head,
+ *     lowbit_gemv, lowbit_gemv_accumulate, lowbit_gemv_noalloc, lowbit_ffn
+ *     and lowbit_lm_head,
  *     and the FFN's h in its workspace -- must be coarse-grained device
  *     memory (hipMalloc, or torch's CUDA allocator).  The library is built
  *     with -munsafe-fp-atomics: on fine-grained or host-coherent memory
@@ -107,7 +109,8 @@ typedef enum {
   LOWBIT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned             */
   LOWBIT_ERR_UNSUPPORTED = 4, /* valid request this build does not implement */
   LOWBIT_ERR_HIP = 5,         /* a HIP call or kernel launch failed           */
-  LOWBIT_ERR_WORKSPACE = 6    /* workspace missing or smaller than required  */
+  LOWBIT_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required  */
+  LOWBIT_ERR_SCRATCH = 7      /* needs more than lowbit_gemv_noalloc's scratch */
 } lowbit_status;
 
 /* Library ABI version (this header describes version 1). */
@@ -232,6 +235,25 @@ int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales,
                 int64_t n, int64_t k, const uint16_t* x_fp16, int64_t b,
                 float* y_f32, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
+
+/* Decode GEMV that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, result and errors as
+ * lowbit_gemv without the workspace: the scratch lowbit_gemv keeps in the
+ * workspace lives in a static device array of 1 MiB per GPU, held until
+ * the process ends, so the call needs
+ *     lowbit_gemv_workspace_bytes(fmt, n, k, b) <= 1 MiB
+ * (b <= 2: 2*b*k bytes, k <= 262144 at b = 2; b >= 3: 32*k bytes,
+ * k <= 32768) and returns LOWBIT_ERR_SCRATCH, launching nothing, beyond
+ * that.  It calls no allocator.  Every call on one GPU uses the same array:
+ * calls that overlap on one GPU (other streams, other host threads) race;
+ * calls ordered on one stream do not.  Nothing in the array needs to start
+ * at zero (the first kernel writes what the second reads, and zeroes y).
+ * The array's device address is looked up once per device, on the first
+ * call made with that device current. */
+int lowbit_gemv_noalloc(int fmt, const void* codes, const uint16_t* scales,
+                        int64_t n, int64_t k, const uint16_t* x_fp16, int64_t b,
+                        float* y_f32, hipStream_t stream);
 
 /* Prefill GEMM  [P2 "Rendimiento ...": prefill is compute-bound].
  *   Y[i][n] = RNE_bf16( sum_g s[n][g] * sum_{k in g} X[i][k] * t[n][k] )

@@ -16,7 +16,7 @@ from bit_matmul_lowbit_amd import lowbit
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lowbit.h")
 
-OK, ARG, SHAPE, ALIGN, UNSUP, HIP, WS = 0, 1, 2, 3, 4, 5, 6
+OK, ARG, SHAPE, ALIGN, UNSUP, HIP, WS, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 Q1, T2 = 1, 2
 
 
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.lowbit_version() == 1
-    for s in range(7):
+    for s in range(8):
         assert lowbit.status_str(s) != "unknown status"
     assert lowbit.status_str(99) == "unknown status"
 
@@ -229,6 +229,23 @@ def test_binding_rejects_short_buffers(lib):
         lowbit._need_numel(torch.empty(3, 7), 22, "out")
     with pytest.raises(ValueError):
         lowbit._need_shape(torch.empty(7, 3), (3, 7), "out")
+
+
+def test_noalloc_limits_are_checked_on_the_host(lib):
+    # lowbit_gemv_noalloc rejects, before touching any device, a request whose
+    # scratch exceeds its 1 MiB static array (the pointers here are never
+    # dereferenced)
+    good = ctypes.c_void_p(1 << 20)
+    st = ctypes.c_void_p(0)
+    assert lib.lowbit_gemv_noalloc(Q1, good, good, 16, 65536, good, 3, good, st) == SCRATCH
+    assert lib.lowbit_gemv_noalloc(T2, good, good, 16, 1 << 19, good, 2, good, st) == SCRATCH
+    assert lib.lowbit_gemv_noalloc(T2, good, good, 16, 128, good, 9, good, st) == ARG
+    assert lib.lowbit_gemv_noalloc(T2, good, good, 16, 130, good, 1, good, st) == SHAPE
+    assert lib.lowbit_gemv_noalloc(T2, ctypes.c_void_p(8), good, 16, 128, good, 1, good, st) == ALIGN
+    assert lib.lowbit_gemv_noalloc(3, good, good, 16, 128, good, 1, good, st) == ARG
+    # the limit sits where the header says: 2*b*k bytes for b <= 2, 32*k for b >= 3
+    for b, k in ((1, 1 << 19), (2, 1 << 18), (3, 1 << 15), (8, 1 << 15)):
+        assert lowbit.lowbit_gemv_workspace_bytes("q1", 16, k, b) == 1 << 20
 
 
 def test_probe_header_and_exports(lib):
