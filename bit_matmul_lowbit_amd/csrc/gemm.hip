@@ -6,7 +6,11 @@
 // [P1] 7minutos.es tutorial, section 7: bit 0 -> -s, bit 1 -> +s.
 // [P2] "Como funciona la compresion": w = s * t, t in {-1, 0, +1}.
 //
-// Tiling: a team of WM x WN waves owns a BM x BN output tile (128 x 128 and
+// Two kernels.  gemm_team_kernel (further below) takes shapes whose
+// 128 x 96 tiles fill whole rounds of the CUs, such as the ternary pp512
+// one; gemm_kernel takes the rest.
+//
+// gemm_kernel tiling: a team of WM x WN waves owns a BM x BN output tile (128 x 128 and
 // 64 x 64 with 2 x 2 waves, 128 x 96 with 4 x 3); each wave's tile is made of
 // 32x32 blocks of the 32x32x16 BF16 matrix-core instruction.  The K loop
 // steps one scale group (128) at a time through LDS:
@@ -588,6 +592,398 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     }
 }
 
+// ---------------------------------------------------------------------------
+// Team kernel.  One work-group per CU computes a BM x BN tile with KT
+// K-teams of WM x WN waves; team t takes the scale groups g = t (mod KT) and
+// the teams' sums are added through LDS at the end.  Each wave owns BI x BJ
+// blocks of 32 x 32 (a 32 x 96 or 32 x 64 wave tile reads 1.33 / 1.5 KB of
+// LDS operands per matrix-core instruction, against 2 KB for a lone block),
+// and with two K-teams of four waves, or four of two, eight waves share the
+// CU.  The K loop runs in stages of 64 (half a scale group) so that every
+// team can double-buffer its stage in LDS:
+//   * X[BM][64] BF16 goes straight from memory into LDS (buffer loads to
+//     LDS, one stage ahead), its 16-byte slots XOR-swizzled by the row;
+//   * the codes of W[BN][64] are loaded one stage ahead into registers,
+//     one byte (and for ternary codes the neg byte) per row-chunk, then
+//     expanded to exact BF16 {-1, 0, +1} and written to LDS while the
+//     matrix cores work on the current stage, so each W row is expanded
+//     once per BM rows of X;
+//   * 4 k-steps of 16 per stage accumulate the group's unscaled FP32 sum
+//     C_g (over the group's two stages), then C += s[n][g] * C_g in FP32.
+// One barrier per stage.  The nearest-even rounding to BF16 happens once,
+// at the store.
+// s_waitcnt immediate that waits until at most n memory loads of this wave
+// are outstanding (LDS and export counters left at their maximum)
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+  return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
+}
+// the same, and every LDS access of this wave complete
+__host__ __device__ constexpr int waitcnt_vm_lds(int n) {
+  return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4);
+}
+
+// Work-group barrier between pipeline stages, without __syncthreads()'s
+// release fence: that fence also waits for this wave's loads into LDS that
+// are still in flight for later stages, which the stage wait below leaves
+// outstanding on purpose.  The caller's s_waitcnt makes this wave's LDS
+// writes and its loads for the next stage complete first; the empty asm
+// statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+constexpr int SK = 64;        // k per pipeline stage: half a scale group
+constexpr int kSS = SK / 8;   // 16-byte slots per LDS row of a stage
+
+// LDS slot of 16-byte column c of row r in a stage buffer (128-byte rows).
+// The XOR with (r & 7) ^ ((r >> 3) & 1) puts any 8, and any 16, consecutive
+// rows' copies of one column in distinct 16-byte bank groups, whether the
+// banks span 128 or 256 bytes.
+__device__ __forceinline__ int sslot(int r, int c) {
+  return r * kSS + (c ^ ((r & 7) ^ ((r >> 3) & 1)));
+}
+
+template <int FMT, bool OUT_F32, int BI, int BJ, int WM, int WN, int KT, bool ALL_LIVE>
+__global__ __launch_bounds__(64 * WM * WN * KT, 1) void gemm_team_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y) {
+  constexpr int NWT = WM * WN;        // waves per team
+  constexpr int NT = 64 * NWT;        // threads per team
+  constexpr int BM = 32 * BI * WM, BN = 32 * BJ * WN;
+  constexpr int XI = BM * kSS / 64;   // X loads to LDS per team-stage (64 slots each)
+  static_assert(XI % NWT == 0, "X stage splits evenly over a team's waves");
+  constexpr int XIW = XI / NWT;
+  constexpr int UPT = BN * kSS / NT;  // W row-chunks expanded per thread per stage
+  static_assert((BN * kSS) % NT == 0 && (NT & (NT - 1)) == 0, "W stage splits evenly");
+  static_assert(BN % 16 == 0, "whole row tiles of W");
+  constexpr int CB = Fmt<FMT>::cell_bytes;
+
+  // per team three X stage buffers (loads go out two stages ahead) and two
+  // W stage buffers, all separate variables: a load into one is not taken
+  // to alias the reads of another
+  __shared__ uint4 xs0[KT][BM * kSS];
+  __shared__ uint4 xs1[KT][BM * kSS];
+  __shared__ uint4 xs2[KT][BM * kSS];
+  __shared__ uint4 ws0[KT][BN * kSS];
+  __shared__ uint4 ws1[KT][BN * kSS];
+
+  const int tid = (int)(threadIdx.x & (NT - 1));
+  const int team = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / NT));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, kh = lane >> 5;
+
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int G = (int)(k / BK);
+  const int64_t chunks = k / kChunk;
+  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t xrows = m - m0 < BM ? m - m0 : BM;
+  const int64_t wt0 = n0 / kTileRows;
+  const int64_t wtiles = ntiles - wt0 < BN / 16 ? ntiles - wt0 : BN / 16;
+  // buffer resources over this tile's rows: offsets past them read zeros
+  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(x + m0 * k, xrows * k * 2);
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(codes + wt0 * chunks * CB, wtiles * chunks * CB);
+  const __amdgpu_buffer_rsrc_t sres =
+      buffer_rsrc(scales + wt0 * G * kTileRows, wtiles * G * kTileRows * 2);
+
+  // X: load j of this wave fills slots (wave + NWT j) * 64 + lane of the
+  // team's stage buffer; slot p holds row p / 8, 16-byte column
+  // (p % 8) ^ swizzle(row) of the stage
+  uint32_t xvoff[XIW];
+#pragma unroll
+  for (int j = 0; j < XIW; ++j) {
+    const int p = (wave + NWT * j) * 64 + lane;
+    const int r = p >> 3;
+    const int c = (p & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+    xvoff[j] = (uint32_t)(r * k * 2 + c * 16);
+  }
+  auto dma_x = [&](int stage_k, uint4 (*buf)[BM * kSS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < XIW; ++j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)(&buf[team][0] + (wave + NWT * j) * 64), 16,
+          xvoff[j], stage_k * 2, 0, 0);
+#else
+      (void)buf;
+      (void)stage_k;
+#endif
+    }
+  };
+
+  // W: row-chunk u = tid + NT i of a stage is row u % BN, chunk u / BN.
+  // Its code byte is byte (r % 4) of the dword loaded at r % 16 rounded
+  // down to 4 (whole dwords: a narrower load would be widened right where
+  // it returns, which waits for it there); the byte is picked at use by a
+  // per-lane v_perm selector.
+  uint32_t wvoff[UPT], wsel[UPT];
+  int wdst[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + NT * i;
+    const int r = u % BN, c = u / BN;
+    const uint32_t bj = (uint32_t)(r & 3);
+    wvoff[i] = (uint32_t)(((r >> 4) * chunks + c) * CB + (r & 12));
+    // Q1: byte bj in the low byte of both halves; ternary: pos ^ neg there
+    // and neg in the high byte (the trit_pair layout)
+    wsel[i] = FMT == 1 ? (0x0C000C00u | (bj << 16) | bj)
+                       : (bj | ((4u + bj) << 8) | (bj << 16) | ((4u + bj) << 24));
+    wdst[i] = sslot(r, c);
+  }
+  struct Codes {
+    uint32_t p[UPT], q[UPT];
+  };
+  auto load_codes = [&](int stage_chunk, Codes& cd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      cd.p[i] = __builtin_amdgcn_raw_buffer_load_b32(wres, wvoff[i], stage_chunk * CB, 0);
+      if constexpr (FMT == 2)
+        cd.q[i] = __builtin_amdgcn_raw_buffer_load_b32(wres, wvoff[i] + 16, stage_chunk * CB, 0);
+    }
+  };
+  // expand row-chunk i of a stage into a W buffer
+  auto expand_unit = [&](const Codes& cd, int i, uint4 (*buf)[BN * kSS])
+                         __attribute__((always_inline)) {
+    uint4 e;
+    if constexpr (FMT == 1)
+      e = expand_q1(__builtin_amdgcn_perm(cd.p[i], cd.p[i], wsel[i]));
+    else
+      e = expand_t2(__builtin_amdgcn_perm(cd.q[i], cd.p[i] ^ cd.q[i], wsel[i]));
+    buf[team][wdst[i]] = e;
+  };
+  auto expand = [&](const Codes& cd, uint4 (*buf)[BN * kSS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) expand_unit(cd, i, buf);
+  };
+
+  // scales of this lane's output columns: the dword holding the FP16 value
+  // (whole dwords, as for the codes), shifted into place at use
+  uint32_t svoff[BJ], svsh[BJ];
+  bool nvalid[BJ];
+#pragma unroll
+  for (int bj = 0; bj < BJ; ++bj) {
+    const int nl = wn * (BJ * 32) + bj * 32 + l32;
+    nvalid[bj] = n0 + nl < n;
+    svoff[bj] = (uint32_t)((((nl >> 4) * G) * kTileRows + (nl & 14)) * 2);
+    svsh[bj] = (uint32_t)(nl & 1) * 16;
+  }
+
+  // team-local group gl is group gl * KT + team; past the end a team's
+  // stages load the last group again and add nothing (team-uniform)
+  const int nloc = (G + KT - 1) / KT;
+  auto gclamp = [&](int gl) __attribute__((always_inline)) {
+    const int g = gl * KT + team;
+    return g < G ? g : G - 1;
+  };
+  auto stage_chunk = [&](int j) __attribute__((always_inline)) {
+    return gclamp(j >> 1) * kChunksPerGroup + (j & 1) * kSS;
+  };
+  auto stage_k = [&](int j) __attribute__((always_inline)) { return stage_chunk(j) * kChunk; };
+
+  // acc: the scaled sum (plain floats: element updates of a vector type
+  // cost register copies); cg: the current group's unscaled sum
+  float acc[BI][BJ][16];
+  f32x16 cg[BI][BJ];
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
+
+  auto read_a = [&](uint4 (*buf)[BM * kSS], int s, int bi) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, buf[team][sslot(wm * (BI * 32) + bi * 32 + l32, 2 * s + kh)]);
+  };
+  auto read_b = [&](uint4 (*buf)[BN * kSS], int s, int bj) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, buf[team][sslot(wn * (BJ * 32) + bj * 32 + l32, 2 * s + kh)]);
+  };
+
+  // Pipeline, stage j (phase P = j mod 6, so that every buffer and register
+  // set below is named at compile time):
+  //   X_j in xs[j % 3]; X_{j+1} and X_{j+2} on their way into the others;
+  //   W_j in ws[j % 2]; codes_{j+1}, codes_{j+2} in registers.
+  //   1. load codes_{j+3} into c[j % 3] (codes_j were expanded in stage j-1);
+  //      at the first stage of a group, load the next group's scales;
+  //   2. four k-steps of MFMAs on X_j, W_j;
+  //   3. expand codes_{j+1} into ws[(j+1) % 2] (read last in stage j-1);
+  //   4. at the second stage of a group, acc += s * C_g;
+  //   5. wait for this wave's loads of X_{j+1}, barrier;
+  //   6. load X_{j+3} into xs[j % 3], which every wave has finished reading.
+  Codes c0, c1, c2;
+  const int S = 2 * nloc;
+  auto clampj = [&](int j) __attribute__((always_inline)) { return j < S ? j : S - 1; };
+  // scales of the three groups of an unrolled pass: group q of the pass in
+  // sv[q], loaded at the first stage of the group before it
+  // (FP16 bit patterns, converted at use: a conversion placed next to the
+  // load would wait for it there)
+  uint32_t sv0[BJ], sv1[BJ], sv2[BJ];
+  auto load_scales = [&](int gl, uint32_t (&sv)[BJ]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bj = 0; bj < BJ; ++bj)
+      sv[bj] = __builtin_amdgcn_raw_buffer_load_b32(sres, svoff[bj], gclamp(gl) * kTileRows * 2, 0);
+  };
+  auto scale_f = [&](uint32_t h, int bj) __attribute__((always_inline)) {
+    return nvalid[bj] ? (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> svsh[bj])) : 0.0f;
+  };
+  // memory loads per stage: codes, and X into LDS
+  constexpr int kCodeLoads = UPT * (FMT == 2 ? 2 : 1);
+  // at the end of stage j, loads issued after X_{j+1}'s: codes of two
+  // stages, one set of scales, X_{j+2}
+  constexpr int kVm = 2 * kCodeLoads + BJ + XIW;
+
+  load_codes(stage_chunk(0), c0);
+  dma_x(stage_k(0), xs0);
+  load_codes(stage_chunk(clampj(1)), c1);
+  dma_x(stage_k(clampj(1)), xs1);
+  load_codes(stage_chunk(clampj(2)), c2);
+  dma_x(stage_k(clampj(2)), xs2);
+  load_scales(0, sv0);
+  expand(c0, ws0);
+  // X_0 has landed: loads issued after it are codes_1, X_1, codes_2, X_2 and
+  // the scales
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCodeLoads + 2 * XIW + BJ));
+  __syncthreads();
+
+  // One stage: the matrix-core steps on X_j and W_j, then the expansion of
+  // the next stage's W; at the group's second stage, C += s * C_g.
+#define LOWBIT_TEAM_MFMA(XB, WB, SV, H)                                                       \
+  {                                                                                           \
+    _Pragma("unroll") for (int s = 0; s < SK / 16; ++s) {                                     \
+      bf16x8 a[BI], b[BJ];                                                                    \
+      _Pragma("unroll") for (int bi = 0; bi < BI; ++bi) a[bi] = read_a(XB, s, bi);            \
+      _Pragma("unroll") for (int bj = 0; bj < BJ; ++bj) b[bj] = read_b(WB, s, bj);            \
+      _Pragma("unroll") for (int bi = 0; bi < BI; ++bi)                                       \
+      _Pragma("unroll") for (int bj = 0; bj < BJ; ++bj) cg[bi][bj] =                          \
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(                                            \
+              a[bi], b[bj], ((H) == 0 && s == 0) ? (f32x16){} : cg[bi][bj], 0, 0, 0);         \
+    }                                                                                         \
+  }
+#define LOWBIT_TEAM_STAGE(P, XB, WB, WN_, CL, CE, SV, SVN)                                     \
+  {                                                                                           \
+    const int j = j0 + (P);                                                                   \
+    constexpr int H = (P) & 1; /* half of the scale group */                                  \
+    load_codes(stage_chunk(clampj(j + 3)), CL);                                               \
+    if constexpr (H == 0) load_scales((j >> 1) + 1, SVN);                                     \
+    LOWBIT_TEAM_MFMA(XB, WB, SV, H)                                                           \
+    expand(CE, WN_);                                                                          \
+    if constexpr (H == 1) {                                                                   \
+      if (ALL_LIVE || (j >> 1) * KT + team < G) {                                             \
+        _Pragma("unroll") for (int bi = 0; bi < BI; ++bi)                                     \
+        _Pragma("unroll") for (int bj = 0; bj < BJ; ++bj) {                                   \
+          const float sc = scale_f(SV[bj], bj);                                               \
+          _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[bi][bj][v] =                     \
+              __builtin_fmaf(sc, cg[bi][bj][v], acc[bi][bj][v]);                              \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(kVm));                                          \
+    stage_barrier();                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    dma_x(stage_k(clampj(j + 3)), XB);                                                        \
+  }
+  int j0 = 0;
+  for (; j0 + 6 <= S; j0 += 6) {
+    LOWBIT_TEAM_STAGE(0, xs0, ws0, ws1, c0, c1, sv0, sv1)
+    LOWBIT_TEAM_STAGE(1, xs1, ws1, ws0, c1, c2, sv0, sv1)
+    LOWBIT_TEAM_STAGE(2, xs2, ws0, ws1, c2, c0, sv1, sv2)
+    LOWBIT_TEAM_STAGE(3, xs0, ws1, ws0, c0, c1, sv1, sv2)
+    LOWBIT_TEAM_STAGE(4, xs1, ws0, ws1, c1, c2, sv2, sv0)
+    LOWBIT_TEAM_STAGE(5, xs2, ws1, ws0, c2, c0, sv2, sv0)
+  }
+  // S is even: 0, 2 or 4 stages remain, starting at phase 0
+  if (j0 < S) {
+    LOWBIT_TEAM_STAGE(0, xs0, ws0, ws1, c0, c1, sv0, sv1)
+    LOWBIT_TEAM_STAGE(1, xs1, ws1, ws0, c1, c2, sv0, sv1)
+  }
+  if (j0 + 2 < S) {
+    LOWBIT_TEAM_STAGE(2, xs2, ws0, ws1, c2, c0, sv1, sv2)
+    LOWBIT_TEAM_STAGE(3, xs0, ws1, ws0, c0, c1, sv1, sv2)
+  }
+#undef LOWBIT_TEAM_STAGE
+#undef LOWBIT_TEAM_MFMA
+  // K-teams 1.. leave their sums in LDS (after every load into it has
+  // landed), team 0 adds them and stores the tile
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // element idx = (team - 1) NE + e of a team's sums, for every thread of
+  // the team, in xs0, then xs1 (idx is a constant once the loops unroll)
+  constexpr int NE = BI * BJ * 16;
+  constexpr int CAPX = KT * BM * kSS * 4 / NT;  // elements per thread in one X buffer
+  static_assert((KT - 1) * NE <= 3 * CAPX, "the team sums fit in the X buffers");
+  auto red = [&](int idx) __attribute__((always_inline)) -> float* {
+    return idx < CAPX       ? reinterpret_cast<float*>(&xs0[0][0]) + idx * NT + tid
+           : idx < 2 * CAPX ? reinterpret_cast<float*>(&xs1[0][0]) + (idx - CAPX) * NT + tid
+                            : reinterpret_cast<float*>(&xs2[0][0]) + (idx - 2 * CAPX) * NT + tid;
+  };
+  if (team > 0) {
+#pragma unroll
+    for (int t = 1; t < KT; ++t) {
+      if (t != team) continue;
+#pragma unroll
+      for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) *red((t - 1) * NE + (bi * BJ + bj) * 16 + v) = acc[bi][bj][v];
+    }
+  }
+  __syncthreads();
+  if (team > 0) return;
+#pragma unroll
+  for (int t = 1; t < KT; ++t)
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[bi][bj][v] += *red((t - 1) * NE + (bi * BJ + bj) * 16 + v);
+
+  // C[i][j] of a 32 x 32 block sits in lane j + 32 ((i / 4) % 2), register
+  // (i % 4) + 4 (i / 8)
+#pragma unroll
+  for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < BJ; ++bj) {
+      if (!nvalid[bj]) continue;
+      const int64_t nn = n0 + wn * (BJ * 32) + bj * 32 + l32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = 8 * (v >> 2) + 4 * kh + (v & 3);
+        const int64_t mm = m0 + wm * (BI * 32) + bi * 32 + i;
+        if (mm >= m) continue;
+        if constexpr (OUT_F32)
+          static_cast<float*>(y)[mm * n + nn] = acc[bi][bj][v];
+        else
+          static_cast<uint16_t*>(y)[mm * n + nn] = f32_to_bf16_rne(acc[bi][bj][v]);
+      }
+    }
+}
+
+template <int FMT, int BI, int BJ, int WM, int WN, int KT>
+hipError_t launch_team(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+                       const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
+  constexpr int BM = 32 * BI * WM, BN = 32 * BJ * WN;
+  const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+  const dim3 block(64 * WM * WN * KT);
+  // every team has a group at every step when KT divides the group count
+  const bool all_live = (k / BK) % KT == 0;
+#define LOWBIT_LAUNCH(OF, AL)                                                                  \
+  hipLaunchKernelGGL((gemm_team_kernel<FMT, OF, BI, BJ, WM, WN, KT, AL>), grid, block, 0, st,  \
+                     codes, scales, x, m, n, k, y)
+  if (out_f32) {
+    if (all_live) LOWBIT_LAUNCH(true, true);
+    else LOWBIT_LAUNCH(true, false);
+  } else {
+    if (all_live) LOWBIT_LAUNCH(false, true);
+    else LOWBIT_LAUNCH(false, false);
+  }
+#undef LOWBIT_LAUNCH
+  return hipGetLastError();
+}
+
 template <int FMT, int BM, int BN, int KT, int WM = 2, int WN = 2>
 hipError_t launch_tile(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                        const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
@@ -605,23 +1001,27 @@ hipError_t launch_tile(const uint8_t* codes, const uint16_t* scales, int64_t n, 
 template <int FMT>
 hipError_t launch_fmt(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                       const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
-  // 128 x 128 tiles when there are enough of them for two per CU, otherwise
-  // 64 x 64 tiles (4x as many work-groups)
-  const int64_t big = ((n + 127) / 128) * ((m + 127) / 128);
-  if (big >= 2 * (int64_t)device_cu_count())
-    return launch_tile<FMT, 128, 128, 1>(codes, scales, n, k, x, m, y, out_f32, st);
-  // 128 x 96 tiles of twelve 32 x 32 waves (one work-group per CU, three
-  // waves per SIMD) when they fill whole rounds of the CUs: each W row is
-  // expanded once per 128 rows of X instead of 64, and a tile re-reads less
-  // from LDS per MFMA than four 64 x 64 ones
   const int64_t cus = (int64_t)device_cu_count();
+  // 128 x 128 tiles when there are enough of them for two per CU
+  const int64_t big = ((n + 127) / 128) * ((m + 127) / 128);
+  if (big >= 2 * cus)
+    return launch_tile<FMT, 128, 128, 1>(codes, scales, n, k, x, m, y, out_f32, st);
+  // 128 x 96 tiles when they fill whole rounds of the CUs: the team kernel
+  // (two K-teams of four 32 x 96 waves; the ternary pp512 shape, 4 x 64 =
+  // 256 tiles, ran 24.3 against 26.8 us cold with the 4 x 3-wave kernel
+  // below), or, for a single scale group, twelve 32 x 32 waves (one
+  // work-group per CU, three waves per SIMD): each W row is expanded once
+  // per 128 rows of X instead of 64
   const int64_t t96 = ((n + 95) / 96) * ((m + 127) / 128);
-  if (m >= 128 && t96 >= cus && t96 % cus == 0)
+  if (m >= 128 && t96 >= cus && t96 % cus == 0) {
+    if (k >= 2 * BK)
+      return launch_team<FMT, 1, 3, 4, 1, 2>(codes, scales, n, k, x, m, y, out_f32, st);
     return launch_tile<FMT, 128, 96, 1, 4, 3>(codes, scales, n, k, x, m, y, out_f32, st);
+  }
   // with no more 64 x 64 tiles than CUs, two K-teams per tile (one 8-wave
   // work-group per CU) keep twice as many waves busy
   const int64_t small = ((n + 63) / 64) * ((m + 63) / 64);
-  if (small <= (int64_t)device_cu_count() && k >= 2 * BK)
+  if (small <= cus && k >= 2 * BK)
     return launch_tile<FMT, 64, 64, 2>(codes, scales, n, k, x, m, y, out_f32, st);
   return launch_tile<FMT, 64, 64, 1>(codes, scales, n, k, x, m, y, out_f32, st);
 }

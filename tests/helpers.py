@@ -104,3 +104,31 @@ def oracle_blocks(call, total, axis, block=None):
     with ThreadPoolExecutor(nt) as ex:
         parts = list(ex.map(lambda s0: call(s0, min(block, total - s0)), starts))
     return np.concatenate(parts, axis=axis)
+
+
+GUARD = 4096      # bytes of known pattern on each side of a guarded output
+GUARD_BYTE = 0xA5
+
+
+def guarded(shape, dtype):
+    """(raw, view): `view` is a device tensor of `shape` and `dtype` that sits
+    inside `raw` with GUARD bytes of GUARD_BYTE before and after it (and is
+    filled with GUARD_BYTE itself); 256-byte aligned like torch's own
+    allocations."""
+    import torch
+
+    shape = tuple(shape)
+    n = 1
+    for d in shape:
+        n *= d
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    raw = torch.full((GUARD + nbytes + GUARD,), GUARD_BYTE, dtype=torch.uint8, device="cuda")
+    view = raw[GUARD:GUARD + nbytes].view(dtype).view(shape)
+    return raw, view
+
+
+def guards_intact(raw):
+    """True if the GUARD bytes on both sides still hold GUARD_BYTE."""
+    head = raw[:GUARD].cpu().numpy()
+    tail = raw[-GUARD:].cpu().numpy()
+    return bool((head == GUARD_BYTE).all() and (tail == GUARD_BYTE).all())

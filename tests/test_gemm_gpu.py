@@ -106,12 +106,15 @@ def test_one_hot_rows_read_weights_exactly(fmt):
 # Ragged shapes that reach each tile configuration of the launcher on a
 # 256-CU part: 64 x 64 tiles, one team (600 x 2000); 128 x 96 tiles filling
 # whole rounds of the CUs (500 x 6100: 64 x 4 = 256 tiles, last tile 52
-# columns and 116 rows; 450 x 6144: 4 x 64 tiles), with 1, 2 and 3 K-groups
-# (the group count mod 3 picks how the three-stage ring starts); 128 x 128
-# tiles (2100 x 4100: 561 tiles).  Smaller shapes above take 64 x 64 tiles
-# with two K-teams.
+# columns and 116 rows; 450 x 6144: 4 x 64 tiles): one K-group takes the
+# twelve-wave kernel, more take the team kernel, whose K-teams run
+# half-group stages unrolled six at a time -- 2 groups (two stages per
+# team: a tail only), 3 (the second team's last group is past the end), 6
+# (one unrolled pass), 10 (a pass and a four-stage tail); 128 x 128 tiles
+# (2100 x 4100: 561 tiles).
+# Smaller shapes above take 64 x 64 tiles with two K-teams.
 CONFIG_SHAPES = [(600, 2000, 384), (450, 6144, 128), (500, 6100, 256), (500, 6100, 384),
-                 (2100, 4100, 128)]
+                 (500, 6100, 768), (512, 6144, 1280), (2100, 4100, 128)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
