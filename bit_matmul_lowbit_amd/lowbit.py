@@ -54,6 +54,12 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m bit_matmul_lowbit_amd.build` "
             "(or __graft_entry__.build()); there is no non-HIP fallback")
+    # torch first: it ships its own HIP runtime under the same soname as the
+    # system one the library links against, and whichever is loaded first
+    # serves both.  Loaded the other way round, torch's tensors and the
+    # library's launches end up in different runtimes and every launch fails.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     p, i64, sz, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     sig = {
