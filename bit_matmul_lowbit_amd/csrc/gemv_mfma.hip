@@ -275,6 +275,116 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// One item per work-group, for matrices with no more items than CUs: the
+// item's x operands are staged in LDS once and read from there at each
+// step, so x is read from memory once per work-group instead of once per
+// wave and group, and a wave's registers hold codes and scales only (32
+// fewer than the persistent kernel).  After the groups, the x buffer holds
+// the waves' partial sums (8 batch rows: b <= 8).
+constexpr int kItemMaxGroups = 8;
+constexpr int kItemXBytes = kItemMaxGroups * kSteps * kXStep;
+constexpr int kItemRedBytes = kWaves * 8 * kRedPitch * 4;
+constexpr int kItemLds = kItemXBytes > kItemRedBytes ? kItemXBytes : kItemRedBytes;
+
+template <int FMT>
+struct CodeRegs {
+  uint4 c[GroupRegs<FMT>::kCells];
+  uint4 s[2];
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint4* __restrict__ xw, float* __restrict__ y, int64_t n, int64_t k, int b,
+    int64_t ntiles, int kpieces, int gpp) {
+  __shared__ uint4 lds[kItemLds / 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = (int)(k / kGroup);
+  const int tl = lane & 15, q = lane >> 4;
+  const int64_t cpitch = (k / kChunk) * Fmt<FMT>::cell_bytes;
+  const int64_t spitch = (int64_t)G * kTileRows * 2;
+  constexpr int GB = FMT == 1 ? 256 : 512;
+  const uint32_t voff_c = (uint32_t)(tl * cpitch + q * (GB / 4));
+  const uint32_t voff_s = (uint32_t)(tl * spitch);
+
+  const int64_t item = blockIdx.x;
+  const int64_t T0 = (item / kpieces) * 16;
+  const int g0 = (int)(item % kpieces) * gpp;
+  const int ng = g0 + gpp < G ? gpp : G - g0;  // groups of this item
+  const int64_t here = ntiles - T0 < 16 ? ntiles - T0 : 16;
+  // lanes whose tile is past the end read past their resource: zeros
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + T0 * cpitch, here * cpitch);
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_rsrc(reinterpret_cast<const uint8_t*>(scales) + T0 * spitch, here * spitch);
+  const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(codes, 0);
+
+  // the wave's groups g0 + wave + 4 i (i < 2), loaded first; a group past
+  // the item reads zeros and adds exact zeros
+  CodeRegs<FMT> cr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int gl = wave + kWaves * i;
+    const bool live = gl < ng;
+    const int g = live ? g0 + gl : 0;
+    constexpr int kCells = GroupRegs<FMT>::kCells;
+#pragma unroll
+    for (int c = 0; c < kCells; ++c) cr[i].c[c] = bload(live ? rc : rz, voff_c, g * GB + 16 * c);
+    cr[i].s[0] = bload<0>(live ? rs : rz, voff_s, g * 32);
+    cr[i].s[1] = bload<16>(live ? rs : rz, voff_s, g * 32);
+  }
+  // the item's x operands into LDS: vector (group gl, step j, lane l) at
+  // (gl * kSteps + j) * 64 + l
+  for (int i = threadIdx.x; i < ng * kSteps * 64; i += kThreads)
+    lds[i] = xw[(int64_t)g0 * kSteps * 64 + i];
+  __syncthreads();
+
+  f32x4 acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int gl = wave + kWaves * i;
+    if (i * kWaves >= gpp) break;  // gpp <= 4: one group per wave
+    GroupRegs<FMT> r;
+#pragma unroll
+    for (int c = 0; c < GroupRegs<FMT>::kCells; ++c) r.c[c] = cr[i].c[c];
+    r.s[0] = cr[i].s[0];
+    r.s[1] = cr[i].s[1];
+    // x from LDS (zeros past the item: the codes of such a group are zero
+    // too, and Q1 zero codes expand to -s, so x must be zero there)
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j)
+      r.x[j] = gl < ng ? lds[(gl * kSteps + j) * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
+    group_mfma<FMT>(r, acc);
+  }
+
+  // partial sums of the waves -> LDS (batch rows 0..7) -> one atomic per
+  // (row, batch row)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);
+  if (q < 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(wave * 8 + 4 * q + v) * kRedPitch + r * 16 + tl] = acc[r][v];
+  }
+  __syncthreads();
+  // thread t: row T0 * 16 + t (t = 16 * tile + rho)
+  const int t = threadIdx.x;
+  const int64_t row = T0 * 16 + t;
+  const int rr = (t & 15) * 16 + (t >> 4);
+  if (row < n) {
+    for (int i = 0; i < b; ++i) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += red[(w * 8 + i) * kRedPitch + rr];
+      atomicAdd(y + i * n + row, sum);
+    }
+  }
+}
+
 }  // namespace
 
 int64_t gemv_mfma_workspace_bytes(int64_t k) { return (k / kGroup) * kSteps * kXStep; }
@@ -317,8 +427,22 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scale
   const int64_t nitems = nblocks * kp;
   const int64_t rounds = (nitems + nwg_max - 1) / nwg_max;
   const int64_t nwg = nitems <= 2 * nwg_max ? nitems : (nitems + rounds - 1) / rounds;
-  const dim3 grid((unsigned)nwg);
   const uint4* xw = static_cast<const uint4*>(ws);
+  // no more items than CUs: one item per work-group, x from LDS (ternary
+  // 6144x2048 and 2048x6144 at b = 5: 11.1 -> 9.0 us; the 27B-class
+  // matrices, 340 and 680 items, ran 12-15 % slower this way than with the
+  // persistent kernel below and stay on it)
+  if (gpp <= kItemMaxGroups && nitems <= (int64_t)cus) {
+    const dim3 igrid((unsigned)nitems);
+    if (fmt == 1)
+      hipLaunchKernelGGL(gemv_mfma_item_kernel<1>, igrid, dim3(kThreads), 0, st, codes, scales, xw,
+                         y, n, k, (int)b, ntiles, (int)kp, gpp);
+    else
+      hipLaunchKernelGGL(gemv_mfma_item_kernel<2>, igrid, dim3(kThreads), 0, st, codes, scales, xw,
+                         y, n, k, (int)b, ntiles, (int)kp, gpp);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)nwg);
   if (fmt == 1)
     hipLaunchKernelGGL(gemv_mfma_kernel<1>, grid, dim3(kThreads), 0, st, codes, scales, xw, y, n,
                        k, (int)b, ntiles, (int)kp, gpp, nitems);
