@@ -25,6 +25,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            kRawBufferFlags);
 }
 
+// s_waitcnt immediate that waits until at most n memory loads of this wave
+// are outstanding (LDS and export counters left at their maximum)
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+  return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
+}
+// the same, and every LDS access of this wave complete
+__host__ __device__ constexpr int waitcnt_vm_lds(int n) {
+  return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4);
+}
+
+// Work-group barrier without __syncthreads()'s release fence: that fence
+// also waits for this wave's loads into LDS that are still in flight for
+// later pipeline stages, which the caller leaves outstanding on purpose.
+// The caller's s_waitcnt makes the LDS accesses (and loads) that the other
+// waves need complete first; the empty asm statements keep the compiler
+// from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Code-byte expansion helpers shared by the matrix-core GEMV and the GEMM.
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 

@@ -43,7 +43,7 @@ __device__ __forceinline__ uint4 z_vector(const float* __restrict__ h, int64_t f
 //                 the output of lowbit_silu_mul);
 //   MFMA = true:  the matrix-core GEMV's operand order -- vector i = (group
 //                 g, step j, lane l) holds batch row l % 16, chunk
-//                 16 g + 4 (l / 16) + j, zeros for rows >= b.
+//                 16 g + 4 j + l / 16, zeros for rows >= b.
 template <bool MFMA>
 __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ h, int64_t f,
                                                        int b, uint4* __restrict__ z,
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
       const int l = (int)(i & 63);
       const int64_t gj = i >> 6;
       row = l & 15;
-      chunk = (gj >> 2) * 16 + 4 * (l >> 4) + (gj & 3);
+      chunk = (gj >> 2) * 16 + 4 * (gj & 3) + (l >> 4);
     } else {
       row = (int)(i / cpr);
       chunk = i - (int64_t)row * cpr;

@@ -612,28 +612,6 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
 //     C_g (over the group's two stages), then C += s[n][g] * C_g in FP32.
 // One barrier per stage.  The nearest-even rounding to BF16 happens once,
 // at the store.
-// s_waitcnt immediate that waits until at most n memory loads of this wave
-// are outstanding (LDS and export counters left at their maximum)
-__host__ __device__ constexpr int waitcnt_vm(int n) {
-  return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
-}
-// the same, and every LDS access of this wave complete
-__host__ __device__ constexpr int waitcnt_vm_lds(int n) {
-  return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4);
-}
-
-// Work-group barrier between pipeline stages, without __syncthreads()'s
-// release fence: that fence also waits for this wave's loads into LDS that
-// are still in flight for later stages, which the stage wait below leaves
-// outstanding on purpose.  The caller's s_waitcnt makes this wave's LDS
-// writes and its loads for the next stage complete first; the empty asm
-// statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void stage_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 constexpr int SK = 64;        // k per pipeline stage: half a scale group
 constexpr int kSS = SK / 8;   // 16-byte slots per LDS row of a stage
 

@@ -21,8 +21,10 @@
 // Column l % 16 of B is row rho of tile T0 + l % 16: every lane reads whole
 // 16-byte code cells (16 rows x 8 k) of its own tile, and byte rho of a cell
 // feeds the MFMA of row rho, so one step issues 16 independent MFMAs
-// (rho = 0..15) that share the A operand.  Lane quarter q = l / 16 takes
-// chunks 4q .. 4q + 3 of each 128-weight group (64 / 128 contiguous bytes).
+// (rho = 0..15) that share the A operand.  Step j of a 128-weight group
+// takes chunks 4j .. 4j + 3, lane quarter q = l / 16 chunk 4j + q (the x
+// operands are laid out to match), so the four lanes of a tile read 64
+// contiguous bytes (Q1; 128 for T2) per load.
 //
 // Expansion of a Q1 byte e (bit j <-> k0 + j) into four FP16 pairs: with e
 // in the low byte of both 16-bit halves, a packed 16-bit shift by
@@ -34,10 +36,14 @@
 //
 // Work: an item is (16-tile block, K-piece).  The grid is persistent (two
 // work-groups per CU); work-group w takes items w, w + W, ... in order, so
-// all work-groups sweep the matrix together.  Inside an item the 4 waves
+// all work-groups sweep the matrix together and the loads in flight at any
+// time cover one contiguous stretch of it.  Inside an item the 4 waves
 // take its groups round-robin; their load rings run on across items, and
 // at the end of an item the waves sum their partials through LDS and add
-// them to y with one coalesced FP32 atomic per (row, batch row).
+// them to y with one coalesced FP32 atomic per (row, batch row).  A matrix
+// with no more items than CUs runs one work-group per item instead.  Only
+// lanes of batch rows < b load x (the others read past their resource,
+// which returns zeros with no memory traffic).
 #include "common.h"
 
 namespace lowbit {
@@ -52,6 +58,13 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kSteps = 4;            // 32-k MFMA steps per 128-weight group
 constexpr int kXStep = 64 * 16;      // bytes of A operand per step (64 lanes x 16 B)
 constexpr int kRedPitch = 260;       // LDS pitch per batch row (256 rows + pad)
+constexpr uint32_t kNoLoad = 0x80000000u;  // lane offset past any resource: zeros
+
+// byte offset of a lane's code cell i of a group, from the lane's quarter base
+template <int FMT>
+constexpr int cell_off(int i) {
+  return FMT == 1 ? 64 * i : 128 * (i >> 1) + 16 * (i & 1);
+}
 
 
 template <int SOFF = 0>
@@ -105,7 +118,8 @@ __device__ __forceinline__ void load_group(GroupRegs<FMT>& r, __amdgpu_buffer_rs
   constexpr int GB = FMT == 1 ? 256 : 512;  // code bytes per tile per group
   const int sc = g * GB;
 #pragma unroll
-  for (int i = 0; i < GroupRegs<FMT>::kCells; ++i) r.c[i] = bload(rc, voff_c, sc + 16 * i);
+  for (int i = 0; i < GroupRegs<FMT>::kCells; ++i)
+    r.c[i] = bload(rc, voff_c, sc + cell_off<FMT>(i));
   r.s[0] = bload<0>(rs, voff_s, g * 32);
   r.s[1] = bload<16>(rs, voff_s, g * 32);
 #pragma unroll
@@ -169,13 +183,13 @@ __global__ __launch_bounds__(256) void gemv_mfma_prepare_kernel(const uint16_t* 
   const int64_t stride = (int64_t)gridDim.x * 256;
   zero_f32(y, ycount, gid, stride);
   for (int64_t i = gid; i < nvec; i += stride) {
-    // vector i = (group g, step j, lane l): batch row l % 16, chunk 16 g + 4 (l / 16) + j
+    // vector i = (group g, step j, lane l): batch row l % 16, chunk 16 g + 4 j + l / 16
     const int l = (int)(i & 63);
     const int64_t gj = i >> 6;
     const int64_t g = gj / kSteps;
     const int j = (int)(gj % kSteps);
     const int row = l & 15;
-    const int64_t chunk = g * 16 + 4 * (l >> 4) + j;
+    const int64_t chunk = g * 16 + 4 * j + (l >> 4);
     xw[i] = row < b ? *reinterpret_cast<const uint4*>(x + row * k + chunk * kChunk)
                     : make_uint4(0u, 0u, 0u, 0u);
   }
@@ -194,10 +208,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   const int tl = lane & 15, q = lane >> 4;
   const int64_t cpitch = (k / kChunk) * Fmt<FMT>::cell_bytes;
   const int64_t spitch = (int64_t)G * kTileRows * 2;
-  constexpr int GB = FMT == 1 ? 256 : 512;
-  const uint32_t voff_c = (uint32_t)(tl * cpitch + q * (GB / 4));
+  const uint32_t voff_c = (uint32_t)(tl * cpitch + q * Fmt<FMT>::cell_bytes);
   const uint32_t voff_s = (uint32_t)(tl * spitch);
-  const uint32_t voff_x = (uint32_t)(lane * 16);
+  const uint32_t voff_x = tl < b ? (uint32_t)(lane * 16) : kNoLoad;
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xw, (int64_t)G * kSteps * kXStep);
   const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(xw, 0);  // all loads return zero
 
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_ker
   const int64_t cpitch = (k / kChunk) * Fmt<FMT>::cell_bytes;
   const int64_t spitch = (int64_t)G * kTileRows * 2;
   constexpr int GB = FMT == 1 ? 256 : 512;
-  const uint32_t voff_c = (uint32_t)(tl * cpitch + q * (GB / 4));
+  const uint32_t voff_c = (uint32_t)(tl * cpitch + q * Fmt<FMT>::cell_bytes);
   const uint32_t voff_s = (uint32_t)(tl * spitch);
 
   const int64_t item = blockIdx.x;
@@ -330,14 +343,15 @@ __global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_ker
     const int g = live ? g0 + gl : 0;
     constexpr int kCells = GroupRegs<FMT>::kCells;
 #pragma unroll
-    for (int c = 0; c < kCells; ++c) cr[i].c[c] = bload(live ? rc : rz, voff_c, g * GB + 16 * c);
+    for (int c = 0; c < kCells; ++c)
+      cr[i].c[c] = bload(live ? rc : rz, voff_c, g * GB + cell_off<FMT>(c));
     cr[i].s[0] = bload<0>(live ? rs : rz, voff_s, g * 32);
     cr[i].s[1] = bload<16>(live ? rs : rz, voff_s, g * 32);
   }
   // the item's x operands into LDS: vector (group gl, step j, lane l) at
   // (gl * kSteps + j) * 64 + l
   for (int i = threadIdx.x; i < ng * kSteps * 64; i += kThreads)
-    lds[i] = xw[(int64_t)g0 * kSteps * 64 + i];
+    lds[i] = (i & 15) < b ? xw[(int64_t)g0 * kSteps * 64 + i] : make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
   f32x4 acc[16];
