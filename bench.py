@@ -150,7 +150,10 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
               with_hash=False):
     """Returns dict with step GB/s, ms/step and the mean accumulate-kernel time;
     with_graph adds the per-step time of a HIP graph holding one step per
-    rotated copy (prepare + accumulate, no host work between launches)."""
+    rotated copy (no host work between launches).  A step is one lowbit_gemv
+    call: prepare + accumulate, or for small matrices the single-launch
+    kernel.  The kernel times are those of the two-phase API's accumulate
+    kernel (the table or matrix-core kernel)."""
     import torch
 
     from bit_matmul_lowbit_amd import lowbit, synth
@@ -165,14 +168,9 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
     ws = torch.empty(lowbit.lowbit_gemv_workspace_bytes(fmt, n, k, b), dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         c, s = copies[i % len(copies)]
-        lowbit.lowbit_gemv_prepare(n, k, x, y, ws, stream=st)
-        if ev is not None:
-            ev[0].record(st)
-        lowbit.lowbit_gemv_accumulate(fmt, c, s, n, k, b, y, ws, stream=st)
-        if ev is not None:
-            ev[1].record(st)
+        lowbit.lowbit_gemv(fmt, c, s, n, k, x, out=y, workspace=ws, stream=st)
 
     for i in range(warmup):
         step(i)
@@ -228,8 +226,7 @@ def time_gemv(fmt, n, k, b, seed, steps, warmup, with_kernel_events=True, with_g
             with torch.cuda.graph(g, stream=cap):
                 for i in range(nc):
                     c, s = copies[i]
-                    lowbit.lowbit_gemv_prepare(n, k, x, y, ws)
-                    lowbit.lowbit_gemv_accumulate(fmt, c, s, n, k, b, y, ws)
+                    lowbit.lowbit_gemv(fmt, c, s, n, k, x, out=y, workspace=ws)
         torch.cuda.current_stream().wait_stream(cap)
         g.replay()
         torch.cuda.synchronize()

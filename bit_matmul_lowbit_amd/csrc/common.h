@@ -158,6 +158,17 @@ hipError_t launch_gemv_noalloc(int fmt, const uint8_t* codes, const uint16_t* sc
 
 // decode FFN: SiLU(gate) * up -> FP16, and the whole gated-MLP chain
 hipError_t launch_silu_mul(const float* h, int64_t f, int64_t b, uint16_t* z, hipStream_t st);
+// Single-launch GEMV for small matrices (gemv_small.hip): y = W x written
+// directly (no prepare, workspace or atomics) when gemv_direct_ok(n, k, b).
+constexpr int64_t kDirectMaxWeights = (int64_t)32 << 20;
+bool gemv_direct_ok(int64_t n, int64_t k, int64_t b);
+hipError_t launch_gemv_direct(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                              int64_t k, const uint16_t* x, int64_t b, float* y, hipStream_t st);
+// the same with x = RNE_fp16(SiLU(gate) * up) formed from h = [gate | up]
+// (FP32 [b][2f]); the matrix is n x f
+hipError_t launch_gemv_direct_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                   int64_t n, int64_t f, const float* h, int64_t b, float* y,
+                                   hipStream_t st);
 size_t ffn_workspace_bytes(int64_t k, int64_t f, int64_t b);
 hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scales,
                       const uint8_t* dn_codes, const uint16_t* dn_scales, int64_t k, int64_t f,

@@ -106,6 +106,13 @@ hipError_t launch_ffn(int fmt, const uint8_t* gu_codes, const uint16_t* gu_scale
   char* base = static_cast<char*>(ws);
   void* ws_x = base;
   float* h = reinterpret_cast<float*>(base + align256((int64_t)gemv_workspace_bytes(k, b)));
+  if (gemv_direct_ok(2 * f, k, b) && gemv_direct_ok(k, f, b)) {
+    // small matrices: two single-launch GEMVs that write h and y outright,
+    // the second forming z from h as it loads its activations
+    hipError_t e = launch_gemv_direct(fmt, gu_codes, gu_scales, 2 * f, k, x, b, h, st);
+    if (e != hipSuccess) return e;
+    return launch_gemv_direct_silu(fmt, dn_codes, dn_scales, k, f, h, b, y, st);
+  }
   if (b < kMfmaMinBatch) {
     // table GEMVs: the down GEMV forms z from h in its own table build, so
     // the chain is three launches (prepare zeroes h and y)

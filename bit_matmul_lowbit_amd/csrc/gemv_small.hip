@@ -1,0 +1,224 @@
+// Decode GEMV for small matrices, b = 1 or 2, in ONE launch:
+//   y[i][n] = sum_g s[n][g] * sum_{k in g} t[n][k] * x[i][k]
+//
+// [P2] 7minutos.es, "PrismML lanza Bonsai 27B ...": decode streams every
+//      low-bit matrix once per token ("Rendimiento y decodificacion
+//      especulativa DSpark").
+// [P1] 7minutos.es tutorial, section 7: bit 0 -> -s, bit 1 -> +s.
+// [P5] openclawradar.com, "Bonsai 1.7B ...", "Detalles tecnicos": decode
+//      of the small model was tuned at the level of its matvec / FFN kernels.
+//
+// A matrix of a few MB is latency-bound: the table GEMV spends its time in
+// two dependent launches (prepare, then accumulate), the table build, a
+// K-sliced sweep and FP32 atomics.  Here one work-group owns one 16-row tile
+// over the whole of K and writes its outputs with plain stores, so there is
+// no prepare launch, no workspace, no atomics and no zeroed y:
+//   * wave w takes K-range [512 w, 512 w + 512) (64 chunks of 8 weights);
+//     lane (rho = l % 16, q = l / 16) takes row rho of the tile and chunks
+//     q, q + 4, ..., q + 60 of that range (16 chunks, 4 groups);
+//   * every load of the lane is issued at once: one code dword per chunk
+//     (rows 4 (rho / 4) .. + 3 of the cell; ternary: pos and neg), one scale
+//     dword per group (rows rho & ~1, + 1), and x as 16-byte FP16 vectors;
+//   * the code byte of row rho goes to the low byte of both 16-bit halves
+//     (v_perm), a packed shift and v_bitop3 turn each bit pair into FP16
+//     (+s or -s; ternary also 0) and v_dot2_f32_f16 adds (+-s) x for two
+//     weights at a time into an FP32 sum -- products of two FP16 numbers are
+//     exact in FP32;
+//   * the four quarter lanes of a row are summed across lanes, the waves'
+//     sums through LDS, and y is stored once.
+// The FFN variant (SILU) takes h = [gate | up] (FP32 [b][2k]) instead of x
+// and forms z = RNE_fp16(SiLU(gate) * up) itself: lane l of wave w forms
+// chunk 64 w + l into LDS, from where the lanes that need it read it.
+#include "common.h"
+
+namespace lowbit {
+namespace {
+
+constexpr int kWaveK = 512;           // weights of K per wave
+constexpr int kLaneChunks = 16;       // chunks per lane
+constexpr int kMaxWaves = 16;         // K <= 8192
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ uint32_t dload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ uint4 qload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int p) {
+  return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w;
+}
+
+// per-half arithmetic shift right by 15: 0xFFFF where bit 15 is set, else 0
+__device__ __forceinline__ uint32_t mask15(uint32_t d) {
+  const s16x2 a = __builtin_bit_cast(s16x2, d);
+  return __builtin_bit_cast(uint32_t, (s16x2)(a >> (s16x2){15, 15}));
+}
+
+template <int FMT, int B, bool SILU>
+__global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_direct_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const void* __restrict__ xin, int64_t n, int64_t k, float* __restrict__ y) {
+  constexpr int CB = Fmt<FMT>::cell_bytes;
+  __shared__ uint4 zbuf[SILU ? kMaxWaves * 64 * B : 1];
+  __shared__ float red[kMaxWaves * 16 * B];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = (int)(blockDim.x >> 6);
+  const int rho = lane & 15, q = lane >> 4;
+  const int64_t tile = blockIdx.x;
+  const int64_t nch = k / kChunk;
+  const int64_t G = k / kGroup;
+  const int c0 = wave * (kWaveK / kChunk);  // first chunk of the wave
+  // chunks past k (last wave of a k that is not a multiple of 512) read as
+  // zeros: codes and scales past their resource, x by the kNoLoad offset
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + tile * nch * CB, nch * CB);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + tile * G * 16, G * 32);
+  constexpr uint32_t kNoLoad = 0x80000000u;
+
+  uint32_t cw[kLaneChunks], nwd[FMT == 2 ? kLaneChunks : 1], sw[kLaneChunks / 4];
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    const uint32_t off = (uint32_t)((c0 + q + 4 * i) * CB + (rho & 12));
+    cw[i] = dload(rc, off);
+    if constexpr (FMT == 2) nwd[i] = dload(rc, off + 16);
+  }
+#pragma unroll
+  for (int j = 0; j < kLaneChunks / 4; ++j)
+    sw[j] = dload(rs, (uint32_t)(((c0 / 16 + j) * 16 + (rho & 14)) * 2));
+
+  uint4 xv[SILU ? 1 : kLaneChunks][B];
+  if constexpr (SILU) {
+    // z of chunk c0 + lane, all batch rows, into LDS (zeros past k)
+    const float* h = static_cast<const float*>(xin);
+    const int64_t c = c0 + lane;
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      if (c < nch) {
+        const float4* g4 = reinterpret_cast<const float4*>(h + bi * 2 * k + c * 8);
+        const float4* u4 = reinterpret_cast<const float4*>(h + bi * 2 * k + k + c * 8);
+        const float4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
+        const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+        const float uv[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+        z = silu_mul8(gv, uv);
+      }
+      zbuf[(wave * 64 + lane) * B + bi] = z;
+    }
+    __syncthreads();
+  } else {
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xin, B * k * 2);
+#pragma unroll
+    for (int i = 0; i < kLaneChunks; ++i) {
+      const int c = c0 + q + 4 * i;
+#pragma unroll
+      for (int bi = 0; bi < B; ++bi)
+        xv[i][bi] = qload(rx, c < nch ? (uint32_t)((bi * k + c * 8) * 2) : kNoLoad);
+    }
+  }
+
+  // byte rho & 3 of a code dword in the low byte of both halves; the scale
+  // of row rho in both halves
+  const uint32_t bsel = 0x0C000C00u | ((uint32_t)(rho & 3) << 16) | (uint32_t)(rho & 3);
+  const uint32_t ssel = (rho & 1) ? 0x03020302u : 0x01000100u;
+  float acc[B];
+#pragma unroll
+  for (int bi = 0; bi < B; ++bi) acc[bi] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kLaneChunks; ++i) {
+    const uint32_t ss = __builtin_amdgcn_perm(sw[i / 4], sw[i / 4], ssel);
+    uint4 xi[B];
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      if constexpr (SILU) xi[bi] = zbuf[(wave * 64 + q + 4 * i) * B + bi];
+      else xi[bi] = xv[i][bi];
+    }
+    if constexpr (FMT == 1) {
+      const uint32_t d = __builtin_amdgcn_perm(cw[i], cw[i], bsel);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t sh = ((uint32_t)(14 - 2 * p) << 16) | (uint32_t)(15 - 2 * p);
+        const uint32_t a = ss ^ (~pk_shl(d, sh) & kSignBits);
+#pragma unroll
+        for (int bi = 0; bi < B; ++bi) acc[bi] = dot2(a, word(xi[bi], p), acc[bi]);
+      }
+    } else {
+      const uint32_t dq = __builtin_amdgcn_perm(nwd[i], nwd[i], bsel);        // neg
+      const uint32_t dn = __builtin_amdgcn_perm(cw[i] ^ nwd[i], cw[i] ^ nwd[i], bsel);  // nonzero
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t sh = ((uint32_t)(14 - 2 * p) << 16) | (uint32_t)(15 - 2 * p);
+        const uint32_t a = (ss ^ (pk_shl(dq, sh) & kSignBits)) & mask15(pk_shl(dn, sh));
+#pragma unroll
+        for (int bi = 0; bi < B; ++bi) acc[bi] = dot2(a, word(xi[bi], p), acc[bi]);
+      }
+    }
+  }
+  // quarter lanes of a row, then the waves
+#pragma unroll
+  for (int bi = 0; bi < B; ++bi) {
+    acc[bi] += __shfl_xor(acc[bi], 16);
+    acc[bi] += __shfl_xor(acc[bi], 32);
+  }
+  if (q == 0) {
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) red[wave * 16 * B + bi * 16 + rho] = acc[bi];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 16 * B) {
+    float sum = 0.0f;
+    for (int w = 0; w < nw; ++w) sum += red[w * 16 * B + t];
+    const int64_t row = tile * kTileRows + (t & 15);
+    if (row < n) y[(t >> 4) * n + row] = sum;
+  }
+}
+
+template <int FMT, int B, bool SILU>
+hipError_t launch_direct(const uint8_t* codes, const uint16_t* scales, const void* xin, int64_t n,
+                         int64_t k, float* y, hipStream_t st) {
+  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
+  const int nw = (int)((k + kWaveK - 1) / kWaveK);
+  hipLaunchKernelGGL((gemv_direct_kernel<FMT, B, SILU>), dim3((unsigned)ntiles), dim3(64 * nw), 0,
+                     st, codes, scales, xin, n, k, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemv_direct_ok(int64_t n, int64_t k, int64_t b) {
+  if (b < 1 || b > 2) return false;
+  if (k > (b == 1 ? 8192 : 4096)) return false;
+  return n * k <= kDirectMaxWeights;
+}
+
+hipError_t launch_gemv_direct(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                              int64_t k, const uint16_t* x, int64_t b, float* y, hipStream_t st) {
+  if (fmt == 1)
+    return b == 1 ? launch_direct<1, 1, false>(codes, scales, x, n, k, y, st)
+                  : launch_direct<1, 2, false>(codes, scales, x, n, k, y, st);
+  return b == 1 ? launch_direct<2, 1, false>(codes, scales, x, n, k, y, st)
+                : launch_direct<2, 2, false>(codes, scales, x, n, k, y, st);
+}
+
+hipError_t launch_gemv_direct_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                   int64_t n, int64_t f, const float* h, int64_t b, float* y,
+                                   hipStream_t st) {
+  if (fmt == 1)
+    return b == 1 ? launch_direct<1, 1, true>(codes, scales, h, n, f, y, st)
+                  : launch_direct<1, 2, true>(codes, scales, h, n, f, y, st);
+  return b == 1 ? launch_direct<2, 1, true>(codes, scales, h, n, f, y, st)
+                : launch_direct<2, 2, true>(codes, scales, h, n, f, y, st);
+}
+
+}  // namespace lowbit

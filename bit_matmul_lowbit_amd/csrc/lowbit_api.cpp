@@ -156,6 +156,13 @@ int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales, int64_t n, i
   if (!shape_ok(n, k)) return LOWBIT_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_fp16) || !aligned16(y_f32))
     return LOWBIT_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lowbit::gemv_workspace_bytes(k, b))
+    return LOWBIT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LOWBIT_ERR_ALIGN;
+  // small matrices: one kernel writes y (the workspace is not touched)
+  if (lowbit::gemv_direct_ok(n, k, b))
+    return hip_status(lowbit::launch_gemv_direct(fmt, static_cast<const uint8_t*>(codes), scales,
+                                                 n, k, x_fp16, b, y_f32, stream));
   const int st = lowbit_gemv_prepare(n, k, x_fp16, b, y_f32, workspace, workspace_bytes, stream);
   if (st != LOWBIT_OK) return st;
   return lowbit_gemv_accumulate(fmt, codes, scales, n, k, b, y_f32, workspace, workspace_bytes,

@@ -57,6 +57,8 @@ size_t gemv_noalloc_scratch_bytes() { return kScratchBytes; }
 hipError_t launch_gemv_noalloc(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                                int64_t k, const uint16_t* x, int64_t b, float* y,
                                hipStream_t st) {
+  // small matrices need no scratch at all
+  if (gemv_direct_ok(n, k, b)) return launch_gemv_direct(fmt, codes, scales, n, k, x, b, y, st);
   void* ws = nullptr;
   hipError_t e = scratch_addr(&ws);
   if (e != hipSuccess) return e;

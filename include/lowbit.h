@@ -227,10 +227,13 @@ int lowbit_gemv_accumulate(int fmt, const void* codes, const uint16_t* scales,
  *   y_f32     : [b][n] row-major FP32 output (device, written)
  *   workspace : at least lowbit_gemv_workspace_bytes(fmt, n, k, b) bytes of
  *               device scratch, contents ignored on entry and clobbered.
- * Equivalent to lowbit_gemv_prepare followed by lowbit_gemv_accumulate.
- * Accumulates in FP32; the summation order is not specified and, because
- * K-slices are combined with atomic adds, may differ from run to run in the
- * last bits. */
+ * Equivalent to lowbit_gemv_prepare followed by lowbit_gemv_accumulate,
+ * except for small matrices (b <= 2, k <= 8192 at b = 1 or 4096 at b = 2,
+ * n * k <= 2^25 weights): those take one kernel in which a work-group owns
+ * whole rows and stores y directly (no atomics; the workspace is then not
+ * touched).  Accumulates in FP32; the summation order is not specified and,
+ * where K-slices are combined with atomic adds, may differ from run to run
+ * in the last bits. */
 int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales,
                 int64_t n, int64_t k, const uint16_t* x_fp16, int64_t b,
                 float* y_f32, void* workspace, size_t workspace_bytes,
@@ -249,6 +252,7 @@ int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales,
  * calls that overlap on one GPU (other streams, other host threads) race;
  * calls ordered on one stream do not.  Nothing in the array needs to start
  * at zero (the first kernel writes what the second reads, and zeroes y).
+ * The small matrices that lowbit_gemv runs in one kernel use no scratch.
  * The array's device address is looked up once per device, on the first
  * call made with that device current. */
 int lowbit_gemv_noalloc(int fmt, const void* codes, const uint16_t* scales,
@@ -302,11 +306,12 @@ size_t lowbit_ffn_workspace_bytes(int fmt, int64_t k, int64_t f, int64_t b);
  *   workspace : at least lowbit_ffn_workspace_bytes(fmt, k, f, b) bytes of
  *               device scratch, contents ignored on entry and clobbered.
  * For b <= 2, z is formed inside the down GEMV (never written out) with the
- * same arithmetic as lowbit_silu_mul.
+ * same arithmetic as lowbit_silu_mul; when both matrices are within
+ * lowbit_gemv's single-kernel limits the chain is those two kernels.
  * Both matrices use format fmt; k and f must be multiples of 128.  As in
- * lowbit_gemv, K-slices are combined with atomic adds, so the last bits of
- * h and y may differ from run to run, and so may a z value that lies on an
- * FP16 rounding boundary. */
+ * lowbit_gemv, K-slices are combined with atomic adds on the larger
+ * shapes, so the last bits of h and y may differ from run to run, and so
+ * may a z value that lies on an FP16 rounding boundary. */
 int lowbit_ffn(int fmt, const void* gu_codes, const uint16_t* gu_scales,
                const void* dn_codes, const uint16_t* dn_scales, int64_t k, int64_t f,
                const uint16_t* x_fp16, int64_t b, float* y_f32, void* workspace,

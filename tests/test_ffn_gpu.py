@@ -82,8 +82,11 @@ def test_silu_mul_matches_oracle():
 
 
 
+# b <= 2 shapes whose matrices are both small run the two single-launch
+# GEMVs; f = 8320 (> 8192) puts the down matrix past that kernel's limit, so
+# those shapes run the table chain
 SMALL = [(128, 128, 1), (256, 384, 2), (384, 256, 3), (512, 640, 5), (1024, 512, 8),
-         (256, 1024, 1), (640, 256, 4), (2048, 6144, 2)]
+         (256, 1024, 1), (640, 256, 4), (2048, 6144, 2), (256, 8320, 1), (128, 8320, 2)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
@@ -110,8 +113,8 @@ def test_ffn_small_shapes(fmt, k, f, b):
 
 @pytest.mark.parametrize("b", [1, 2, 3])
 def test_ffn_zero_gate_gives_exact_zeros(b):
-    """SiLU(0) * up = 0 exactly, through both z paths (formed in the down
-    GEMV's table build for b <= 2, by its own launch for b >= 3)."""
+    """SiLU(0) * up = 0 exactly, through the z paths (formed by the down
+    GEMV itself for b <= 2, by its own launch for b >= 3)."""
     import torch
 
     say(f"ffn zero gate b={b}")

@@ -68,6 +68,54 @@ def test_small_shapes(fmt, n, k, b):
     assert_close(y, ref, f"{fmt} {n}x{k} b={b}")
 
 
+def _gemv_split(fmt, codes, scales, n, k, x16):
+    """The two-phase API (prepare, then accumulate): always the table kernel
+    (b <= 2) or the matrix-core kernel (b >= 3), whatever the size."""
+    import torch
+
+    b = x16.shape[0]
+    c, s, x = torch.from_numpy(codes).cuda(), dev_u16(scales), dev_u16(x16)
+    y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lowbit.lowbit_gemv_workspace_bytes(fmt, n, k, b), dtype=torch.uint8,
+                     device="cuda")
+    lowbit.lowbit_gemv_prepare(n, k, x, y, ws)
+    lowbit.lowbit_gemv_accumulate(fmt, c, s, n, k, b, y, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+# lowbit_gemv sends these b <= 2 shapes to the single-launch kernel; the
+# two-phase calls keep the table kernel covered at the same shapes
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("b", [1, 2])
+def test_small_shapes_two_phase(fmt, n, k, b):
+    say(f"gemv two-phase {fmt} n={n} k={k} b={b}")
+    g, codes, scales = _make(fmt, n, k, 650 + n + k + b)
+    x = synth.fp16_normal(g, (b, k))
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.gemv(f, codes, scales, n, k, x)
+    assert_close(_gemv_split(fmt, codes, scales, n, k, x), ref, f"two-phase {fmt} {n}x{k} b={b}")
+
+
+# the single-launch kernel's limits: 16 waves (k = 8192) at b = 1, 8 waves
+# (k = 4096) at b = 2, n * k = 32 Mi weights; and the first shapes past them
+# (table kernel)
+EDGES = [(40, 8192, 1), (40, 4096, 2), (40, 8320, 1), (40, 4224, 2), (4096, 8192, 1),
+         (4112, 8192, 1), (17, 7808, 1), (2049, 4096, 2)]
+
+
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("n,k,b", EDGES)
+def test_single_launch_limits(fmt, n, k, b):
+    say(f"gemv limits {fmt} n={n} k={k} b={b}")
+    g, codes, scales = _make(fmt, n, k, 660 + n + k + b)
+    x = synth.fp16_normal(g, (b, k))
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    ref = oracle.gemv(f, codes, scales, n, k, x)
+    assert_close(_gemv(fmt, codes, scales, n, k, x), ref, f"{fmt} {n}x{k} b={b}")
+
+
 def test_zero_codes_and_zero_scales():
     n, k = 40, 512
     say("gemv zero codes / zero scales")
