@@ -161,6 +161,7 @@ hipError_t launch_silu_mul(const float* h, int64_t f, int64_t b, uint16_t* z, hi
 // Single-launch GEMV for small matrices (gemv_small.hip): y = W x written
 // directly (no prepare, workspace or atomics) when gemv_direct_ok(n, k, b).
 constexpr int64_t kDirectMaxWeights = (int64_t)32 << 20;
+constexpr int64_t kDirectBatchWeight = 4;  // b >= 3: n * k * b <= 4 * kDirectMaxWeights
 bool gemv_direct_ok(int64_t n, int64_t k, int64_t b);
 hipError_t launch_gemv_direct(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                               int64_t k, const uint16_t* x, int64_t b, float* y, hipStream_t st);

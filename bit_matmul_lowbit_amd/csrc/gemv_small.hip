@@ -1,4 +1,4 @@
-// Decode GEMV for small matrices, b = 1 or 2, in ONE launch:
+// Decode GEMV for small matrices, b = 1..8, in ONE launch:
 //   y[i][n] = sum_g s[n][g] * sum_{k in g} t[n][k] * x[i][k]
 //
 // [P2] 7minutos.es, "PrismML lanza Bonsai 27B ...": decode streams every
@@ -18,7 +18,9 @@
 //     q, q + 4, ..., q + 60 of that range (16 chunks, 4 groups);
 //   * every load of the lane is issued at once: one code dword per chunk
 //     (rows 4 (rho / 4) .. + 3 of the cell; ternary: pos and neg), one scale
-//     dword per group (rows rho & ~1, + 1), and x as 16-byte FP16 vectors;
+//     dword per group (rows rho & ~1, + 1), and, for b <= 2, x as 16-byte
+//     FP16 vectors; for b >= 3 (k <= 4096) the work-group copies x into LDS
+//     once while those loads are in flight, and lanes read it from there;
 //   * the code byte of row rho goes to the low byte of both 16-bit halves
 //     (v_perm), a packed shift and v_bitop3 turn each bit pair into FP16
 //     (+s or -s; ternary also 0) and v_dot2_f32_f16 adds (+-s) x for two
@@ -65,13 +67,20 @@ __device__ __forceinline__ uint32_t mask15(uint32_t d) {
   return __builtin_bit_cast(uint32_t, (s16x2)(a >> (s16x2){15, 15}));
 }
 
+constexpr int kMaxKLds = 4096;        // k limit when x (or z) sits in LDS, b >= 3
+
+template <int B>
+constexpr int max_waves() { return B <= 2 ? kMaxWaves : kMaxKLds / kWaveK; }
+
 template <int FMT, int B, bool SILU>
-__global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_direct_kernel(
+__global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const void* __restrict__ xin, int64_t n, int64_t k, float* __restrict__ y) {
   constexpr int CB = Fmt<FMT>::cell_bytes;
-  __shared__ uint4 zbuf[SILU ? kMaxWaves * 64 * B : 1];
-  __shared__ float red[kMaxWaves * 16 * B];
+  constexpr bool XLDS = !SILU && B >= 3;  // x staged in LDS
+  __shared__ uint4 zbuf[SILU ? max_waves<B>() * 64 * B : 1];
+  __shared__ uint4 xbuf[XLDS ? B * kMaxKLds / 8 : 1];
+  __shared__ float red[max_waves<B>() * 16 * B];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = (int)(blockDim.x >> 6);
@@ -97,8 +106,17 @@ __global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_direct_kernel(
   for (int j = 0; j < kLaneChunks / 4; ++j)
     sw[j] = dload(rs, (uint32_t)(((c0 / 16 + j) * 16 + (rho & 14)) * 2));
 
-  uint4 xv[SILU ? 1 : kLaneChunks][B];
-  if constexpr (SILU) {
+  uint4 xv[SILU || XLDS ? 1 : kLaneChunks][B];
+  const int pitch = nw * 64;  // chunks per x row in LDS: zeros past k
+  if constexpr (XLDS) {
+    // x [B][k] FP16 into LDS, 16 bytes per thread and round
+    const uint4* x4 = static_cast<const uint4*>(xin);
+    for (int v = threadIdx.x; v < B * pitch; v += blockDim.x) {
+      const int bi = v / pitch, c = v - bi * pitch;
+      xbuf[v] = c < nch ? x4[bi * nch + c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+  } else if constexpr (SILU) {
     // z of chunk c0 + lane, all batch rows, into LDS (zeros past k)
     const float* h = static_cast<const float*>(xin);
     const int64_t c = c0 + lane;
@@ -140,8 +158,13 @@ __global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_direct_kernel(
     uint4 xi[B];
 #pragma unroll
     for (int bi = 0; bi < B; ++bi) {
-      if constexpr (SILU) xi[bi] = zbuf[(wave * 64 + q + 4 * i) * B + bi];
-      else xi[bi] = xv[i][bi];
+      if constexpr (SILU) {
+        xi[bi] = zbuf[(wave * 64 + q + 4 * i) * B + bi];
+      } else if constexpr (XLDS) {
+        xi[bi] = xbuf[bi * pitch + c0 + q + 4 * i];
+      } else {
+        xi[bi] = xv[i][bi];
+      }
     }
     if constexpr (FMT == 1) {
       const uint32_t d = __builtin_amdgcn_perm(cw[i], cw[i], bsel);
@@ -175,8 +198,8 @@ __global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_direct_kernel(
     for (int bi = 0; bi < B; ++bi) red[wave * 16 * B + bi * 16 + rho] = acc[bi];
   }
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < 16 * B) {
+  // 16 B outputs; a work-group of one wave (k <= 512) has fewer threads
+  for (int t = threadIdx.x; t < 16 * B; t += blockDim.x) {
     float sum = 0.0f;
     for (int w = 0; w < nw; ++w) sum += red[w * 16 * B + t];
     const int64_t row = tile * kTileRows + (t & 15);
@@ -194,31 +217,40 @@ hipError_t launch_direct(const uint8_t* codes, const uint16_t* scales, const voi
   return hipGetLastError();
 }
 
+template <int FMT, bool SILU>
+hipError_t launch_direct_b(const uint8_t* codes, const uint16_t* scales, const void* xin,
+                           int64_t n, int64_t k, int64_t b, float* y, hipStream_t st) {
+  switch (b) {
+    case 1: return launch_direct<FMT, 1, SILU>(codes, scales, xin, n, k, y, st);
+    case 2: return launch_direct<FMT, 2, SILU>(codes, scales, xin, n, k, y, st);
+    case 3: return launch_direct<FMT, 3, SILU>(codes, scales, xin, n, k, y, st);
+    case 4: return launch_direct<FMT, 4, SILU>(codes, scales, xin, n, k, y, st);
+    case 5: return launch_direct<FMT, 5, SILU>(codes, scales, xin, n, k, y, st);
+    case 6: return launch_direct<FMT, 6, SILU>(codes, scales, xin, n, k, y, st);
+    case 7: return launch_direct<FMT, 7, SILU>(codes, scales, xin, n, k, y, st);
+    default: return launch_direct<FMT, 8, SILU>(codes, scales, xin, n, k, y, st);
+  }
+}
+
 }  // namespace
 
 bool gemv_direct_ok(int64_t n, int64_t k, int64_t b) {
-  if (b < 1 || b > 2) return false;
-  if (k > (b == 1 ? 8192 : 4096)) return false;
-  return n * k <= kDirectMaxWeights;
+  if (b < 1 || b > 8) return false;
+  if (k > (b == 1 ? 8192 : b == 2 ? 4096 : kMaxKLds)) return false;
+  return n * k * (b <= 2 ? 1 : b) <= kDirectMaxWeights * (b <= 2 ? 1 : kDirectBatchWeight);
 }
 
 hipError_t launch_gemv_direct(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                               int64_t k, const uint16_t* x, int64_t b, float* y, hipStream_t st) {
-  if (fmt == 1)
-    return b == 1 ? launch_direct<1, 1, false>(codes, scales, x, n, k, y, st)
-                  : launch_direct<1, 2, false>(codes, scales, x, n, k, y, st);
-  return b == 1 ? launch_direct<2, 1, false>(codes, scales, x, n, k, y, st)
-                : launch_direct<2, 2, false>(codes, scales, x, n, k, y, st);
+  return fmt == 1 ? launch_direct_b<1, false>(codes, scales, x, n, k, b, y, st)
+                  : launch_direct_b<2, false>(codes, scales, x, n, k, b, y, st);
 }
 
 hipError_t launch_gemv_direct_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
                                    int64_t n, int64_t f, const float* h, int64_t b, float* y,
                                    hipStream_t st) {
-  if (fmt == 1)
-    return b == 1 ? launch_direct<1, 1, true>(codes, scales, h, n, f, y, st)
-                  : launch_direct<1, 2, true>(codes, scales, h, n, f, y, st);
-  return b == 1 ? launch_direct<2, 1, true>(codes, scales, h, n, f, y, st)
-                : launch_direct<2, 2, true>(codes, scales, h, n, f, y, st);
+  return fmt == 1 ? launch_direct_b<1, true>(codes, scales, h, n, f, b, y, st)
+                  : launch_direct_b<2, true>(codes, scales, h, n, f, b, y, st);
 }
 
 }  // namespace lowbit

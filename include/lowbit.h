@@ -228,10 +228,10 @@ int lowbit_gemv_accumulate(int fmt, const void* codes, const uint16_t* scales,
  *   workspace : at least lowbit_gemv_workspace_bytes(fmt, n, k, b) bytes of
  *               device scratch, contents ignored on entry and clobbered.
  * Equivalent to lowbit_gemv_prepare followed by lowbit_gemv_accumulate,
- * except for small matrices (b <= 2, k <= 8192 at b = 1 or 4096 at b = 2,
- * n * k <= 2^25 weights): those take one kernel in which a work-group owns
- * whole rows and stores y directly (no atomics; the workspace is then not
- * touched).  Accumulates in FP32; the summation order is not specified and,
+ * except for small matrices (k <= 8192 at b = 1, k <= 4096 at b >= 2, and
+ * n * k <= 2^25 weights at b <= 2 or n * k * b <= 2^27 at b >= 3): those
+ * take one kernel in which a work-group owns whole rows and stores y
+ * directly (no atomics; the workspace is then not touched).  Accumulates in FP32; the summation order is not specified and,
  * where K-slices are combined with atomic adds, may differ from run to run
  * in the last bits. */
 int lowbit_gemv(int fmt, const void* codes, const uint16_t* scales,
@@ -305,9 +305,11 @@ size_t lowbit_ffn_workspace_bytes(int fmt, int64_t k, int64_t f, int64_t b);
  *   y_f32     : [b][k] FP32 (device, written)
  *   workspace : at least lowbit_ffn_workspace_bytes(fmt, k, f, b) bytes of
  *               device scratch, contents ignored on entry and clobbered.
- * For b <= 2, z is formed inside the down GEMV (never written out) with the
- * same arithmetic as lowbit_silu_mul; when both matrices are within
- * lowbit_gemv's single-kernel limits the chain is those two kernels.
+ * When both matrices are within lowbit_gemv's single-kernel limits the
+ * chain is two kernels, the second forming z itself; otherwise, for b <= 2,
+ * z is formed inside the down GEMV, and for b >= 3 by its own launch.  z
+ * is never written out except by that launch, and always with the
+ * arithmetic of lowbit_silu_mul.
  * Both matrices use format fmt; k and f must be multiples of 128.  As in
  * lowbit_gemv, K-slices are combined with atomic adds on the larger
  * shapes, so the last bits of h and y may differ from run to run, and so

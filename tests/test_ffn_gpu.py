@@ -82,11 +82,13 @@ def test_silu_mul_matches_oracle():
 
 
 
-# b <= 2 shapes whose matrices are both small run the two single-launch
-# GEMVs; f = 8320 (> 8192) puts the down matrix past that kernel's limit, so
-# those shapes run the table chain
+# shapes whose matrices are both small run the two single-launch GEMVs;
+# f = 8320 (> 8192) or, for b >= 2, f = 4224 (> 4096) puts the down matrix
+# past that kernel's limit, so those shapes run the table (b <= 2) or
+# matrix-core (b >= 3) chain
 SMALL = [(128, 128, 1), (256, 384, 2), (384, 256, 3), (512, 640, 5), (1024, 512, 8),
-         (256, 1024, 1), (640, 256, 4), (2048, 6144, 2), (256, 8320, 1), (128, 8320, 2)]
+         (256, 1024, 1), (640, 256, 4), (2048, 6144, 2), (256, 8320, 1), (128, 8320, 2),
+         (256, 4224, 3), (128, 4224, 5), (256, 4224, 8)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])

@@ -84,11 +84,12 @@ def _gemv_split(fmt, codes, scales, n, k, x16):
     return y.cpu().numpy().astype(np.float64)
 
 
-# lowbit_gemv sends these b <= 2 shapes to the single-launch kernel; the
-# two-phase calls keep the table kernel covered at the same shapes
+# lowbit_gemv sends most of these shapes to the single-launch kernel; the
+# two-phase calls keep the table (b <= 2) and matrix-core (b >= 3) kernels
+# covered at the same shapes
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
 @pytest.mark.parametrize("n,k", SHAPES)
-@pytest.mark.parametrize("b", [1, 2])
+@pytest.mark.parametrize("b", [1, 2, 3, 5, 8])
 def test_small_shapes_two_phase(fmt, n, k, b):
     say(f"gemv two-phase {fmt} n={n} k={k} b={b}")
     g, codes, scales = _make(fmt, n, k, 650 + n + k + b)
@@ -99,10 +100,11 @@ def test_small_shapes_two_phase(fmt, n, k, b):
 
 
 # the single-launch kernel's limits: 16 waves (k = 8192) at b = 1, 8 waves
-# (k = 4096) at b = 2, n * k = 32 Mi weights; and the first shapes past them
-# (table kernel)
+# (k = 4096) at b >= 2, n * k <= 32 Mi weights (b <= 2) or n * k * b <= 128 Mi
+# (b >= 3); and the first shapes past them (table / matrix-core kernels)
 EDGES = [(40, 8192, 1), (40, 4096, 2), (40, 8320, 1), (40, 4224, 2), (4096, 8192, 1),
-         (4112, 8192, 1), (17, 7808, 1), (2049, 4096, 2)]
+         (4112, 8192, 1), (17, 7808, 1), (2049, 4096, 2), (40, 4096, 8), (40, 4224, 3),
+         (6544, 4096, 5), (6600, 4096, 5), (7, 128, 8), (33, 640, 6)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
