@@ -11,8 +11,9 @@
 // A matrix of a few MB is latency-bound: the table GEMV spends its time in
 // two dependent launches (prepare, then accumulate), the table build, a
 // K-sliced sweep and FP32 atomics.  Here one work-group owns one 16-row tile
-// over the whole of K and writes its outputs with plain stores, so there is
-// no prepare launch, no workspace, no atomics and no zeroed y:
+// (or, for a matrix with fewer tiles than twice the CUs, half a tile) over
+// the whole of K and writes its outputs with plain stores, so there is no
+// prepare launch, no workspace, no atomics and no zeroed y:
 //   * wave w takes K-range [512 w, 512 w + 512) (64 chunks of 8 weights);
 //     lane (rho = l % 16, q = l / 16) takes row rho of the tile and chunks
 //     q, q + 4, ..., q + 60 of that range (16 chunks, 4 groups);
@@ -68,24 +69,33 @@ __device__ __forceinline__ uint32_t mask15(uint32_t d) {
 }
 
 constexpr int kMaxKLds = 4096;        // k limit when x (or z) sits in LDS, b >= 3
+constexpr int kHalfTileBelow = 2;     // half-tile work-groups below this many tiles per CU
 
 template <int B>
 constexpr int max_waves() { return B <= 2 ? kMaxWaves : kMaxKLds / kWaveK; }
 
-template <int FMT, int B, bool SILU>
+// RH = rows per work-group: 16 (a tile), or 8 (half a tile, for matrices
+// with fewer tiles than twice the CUs: twice the work-groups, each lane half
+// the chunks).  Lane (rho, q): row rho of the work-group's RH rows, chunks
+// q, q + QN, ... of the wave's range (QN = 64 / RH lanes per row).
+template <int FMT, int B, bool SILU, int RH>
 __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const void* __restrict__ xin, int64_t n, int64_t k, float* __restrict__ y) {
   constexpr int CB = Fmt<FMT>::cell_bytes;
+  constexpr int QN = 64 / RH;               // lanes per row
+  constexpr int LC = kLaneChunks * 4 / QN;  // chunks per lane
+  static_assert(RH == 16 || RH == 8, "a tile or half a tile per work-group");
   constexpr bool XLDS = !SILU && B >= 3;  // x staged in LDS
   __shared__ uint4 zbuf[SILU ? max_waves<B>() * 64 * B : 1];
   __shared__ uint4 xbuf[XLDS ? B * kMaxKLds / 8 : 1];
-  __shared__ float red[max_waves<B>() * 16 * B];
+  __shared__ float red[max_waves<B>() * RH * B];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = (int)(blockDim.x >> 6);
-  const int rho = lane & 15, q = lane >> 4;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = RH == 16 ? blockIdx.x : blockIdx.x >> 1;
+  const int r0 = RH == 16 ? 0 : (int)(blockIdx.x & 1) * 8;  // first row in the tile
+  const int rho = r0 + (lane % RH), q = lane / RH;             // row in the tile, chunk lane
   const int64_t nch = k / kChunk;
   const int64_t G = k / kGroup;
   const int c0 = wave * (kWaveK / kChunk);  // first chunk of the wave
@@ -95,18 +105,20 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + tile * G * 16, G * 32);
   constexpr uint32_t kNoLoad = 0x80000000u;
 
-  uint32_t cw[kLaneChunks], nwd[FMT == 2 ? kLaneChunks : 1], sw[kLaneChunks / 4];
+  // chunk c0 + q + QN i lies in group c0 / 16 + (q + QN i) / 16 = c0 / 16 + i / (16 / QN)
+  constexpr int IPG = 16 / QN;  // a lane's chunks per group
+  uint32_t cw[LC], nwd[FMT == 2 ? LC : 1], sw[LC / IPG];
 #pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    const uint32_t off = (uint32_t)((c0 + q + 4 * i) * CB + (rho & 12));
+  for (int i = 0; i < LC; ++i) {
+    const uint32_t off = (uint32_t)((c0 + q + QN * i) * CB + (rho & 12));
     cw[i] = dload(rc, off);
     if constexpr (FMT == 2) nwd[i] = dload(rc, off + 16);
   }
 #pragma unroll
-  for (int j = 0; j < kLaneChunks / 4; ++j)
+  for (int j = 0; j < LC / IPG; ++j)
     sw[j] = dload(rs, (uint32_t)(((c0 / 16 + j) * 16 + (rho & 14)) * 2));
 
-  uint4 xv[SILU || XLDS ? 1 : kLaneChunks][B];
+  uint4 xv[SILU || XLDS ? 1 : LC][B];
   const int pitch = nw * 64;  // chunks per x row in LDS: zeros past k
   if constexpr (XLDS) {
     // x [B][k] FP16 into LDS, 16 bytes per thread and round
@@ -137,8 +149,8 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
   } else {
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xin, B * k * 2);
 #pragma unroll
-    for (int i = 0; i < kLaneChunks; ++i) {
-      const int c = c0 + q + 4 * i;
+    for (int i = 0; i < LC; ++i) {
+      const int c = c0 + q + QN * i;
 #pragma unroll
       for (int bi = 0; bi < B; ++bi)
         xv[i][bi] = qload(rx, c < nch ? (uint32_t)((bi * k + c * 8) * 2) : kNoLoad);
@@ -153,15 +165,15 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
 #pragma unroll
   for (int bi = 0; bi < B; ++bi) acc[bi] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kLaneChunks; ++i) {
-    const uint32_t ss = __builtin_amdgcn_perm(sw[i / 4], sw[i / 4], ssel);
+  for (int i = 0; i < LC; ++i) {
+    const uint32_t ss = __builtin_amdgcn_perm(sw[i / IPG], sw[i / IPG], ssel);
     uint4 xi[B];
 #pragma unroll
     for (int bi = 0; bi < B; ++bi) {
       if constexpr (SILU) {
-        xi[bi] = zbuf[(wave * 64 + q + 4 * i) * B + bi];
+        xi[bi] = zbuf[(wave * 64 + q + QN * i) * B + bi];
       } else if constexpr (XLDS) {
-        xi[bi] = xbuf[bi * pitch + c0 + q + 4 * i];
+        xi[bi] = xbuf[bi * pitch + c0 + q + QN * i];
       } else {
         xi[bi] = xv[i][bi];
       }
@@ -187,23 +199,24 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
       }
     }
   }
-  // quarter lanes of a row, then the waves
+  // the QN lanes of a row, then the waves
 #pragma unroll
   for (int bi = 0; bi < B; ++bi) {
+    if constexpr (QN == 8) acc[bi] += __shfl_xor(acc[bi], 8);
     acc[bi] += __shfl_xor(acc[bi], 16);
     acc[bi] += __shfl_xor(acc[bi], 32);
   }
   if (q == 0) {
 #pragma unroll
-    for (int bi = 0; bi < B; ++bi) red[wave * 16 * B + bi * 16 + rho] = acc[bi];
+    for (int bi = 0; bi < B; ++bi) red[wave * RH * B + bi * RH + (rho - r0)] = acc[bi];
   }
   __syncthreads();
-  // 16 B outputs; a work-group of one wave (k <= 512) has fewer threads
-  for (int t = threadIdx.x; t < 16 * B; t += blockDim.x) {
+  // RH B outputs; a work-group of one wave (k <= 512) may have fewer threads
+  for (int t = threadIdx.x; t < RH * B; t += blockDim.x) {
     float sum = 0.0f;
-    for (int w = 0; w < nw; ++w) sum += red[w * 16 * B + t];
-    const int64_t row = tile * kTileRows + (t & 15);
-    if (row < n) y[(t >> 4) * n + row] = sum;
+    for (int w = 0; w < nw; ++w) sum += red[w * RH * B + t];
+    const int64_t row = tile * kTileRows + r0 + (t % RH);
+    if (row < n) y[(t / RH) * n + row] = sum;
   }
 }
 
@@ -212,8 +225,12 @@ hipError_t launch_direct(const uint8_t* codes, const uint16_t* scales, const voi
                          int64_t k, float* y, hipStream_t st) {
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
   const int nw = (int)((k + kWaveK - 1) / kWaveK);
-  hipLaunchKernelGGL((gemv_direct_kernel<FMT, B, SILU>), dim3((unsigned)ntiles), dim3(64 * nw), 0,
-                     st, codes, scales, xin, n, k, y);
+  if (ntiles < kHalfTileBelow * (int64_t)device_cu_count())
+    hipLaunchKernelGGL((gemv_direct_kernel<FMT, B, SILU, 8>), dim3((unsigned)(2 * ntiles)),
+                       dim3(64 * nw), 0, st, codes, scales, xin, n, k, y);
+  else
+    hipLaunchKernelGGL((gemv_direct_kernel<FMT, B, SILU, 16>), dim3((unsigned)ntiles),
+                       dim3(64 * nw), 0, st, codes, scales, xin, n, k, y);
   return hipGetLastError();
 }
 
