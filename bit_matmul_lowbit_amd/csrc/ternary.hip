@@ -20,6 +20,7 @@ namespace lowbit {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kQBlock = 128;  // quantiser: chunks per work-group
 
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return max(a & 0xFFFFu, b & 0xFFFFu) | (max(a >> 16, b >> 16) << 16);
@@ -42,13 +43,14 @@ __device__ __forceinline__ bool twice_gt(uint32_t m, uint32_t S) {
 // shuffle), decide their 32 weights, and shift the block's pos and neg code
 // words into place.  Only one block is live at a time, so the kernel keeps
 // enough waves in flight to stream at HBM speed.
-__global__ __launch_bounds__(kBlock) void quantize_t2_kernel(const uint16_t* __restrict__ w,
-                                                             int64_t n, int64_t k,
-                                                             uint8_t* __restrict__ codes,
-                                                             uint16_t* __restrict__ scales) {
+__global__ __launch_bounds__(kQBlock) void quantize_t2_kernel(const uint16_t* __restrict__ w,
+                                                              int64_t n, int64_t k,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint16_t* __restrict__ scales) {
   const int64_t chunks = k / kChunk;
-  const int64_t tile = blockIdx.x;
-  const int64_t c = (int64_t)blockIdx.y * kBlock + threadIdx.x;
+  const int64_t cblocks = (chunks + kQBlock - 1) / kQBlock;
+  const int64_t tile = blockIdx.x / cblocks;
+  const int64_t c = (int64_t)(blockIdx.x - tile * cblocks) * kQBlock + threadIdx.x;
   if (c >= chunks) return;  // whole 16-lane groups leave together
   const int jr = (int)(c % kChunksPerGroup);  // this lane writes the scale of row jr
   uint32_t p0 = 0u, p1 = 0u, p2 = 0u, p3 = 0u, q0 = 0u, q1 = 0u, q2 = 0u, q3 = 0u;
@@ -241,17 +243,19 @@ __global__ __launch_bounds__(kBlock) void base3_to_t2_kernel(const uint8_t* __re
   }
 }
 
+// one work-group per (tile, block of kQBlock chunks), the blocks of a tile
+// consecutive, as for the 1-bit quantiser
 dim3 tile_grid(int64_t n, int64_t k) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t cblocks = (k / kChunk + kBlock - 1) / kBlock;
-  return dim3((unsigned)tiles, (unsigned)cblocks);
+  const int64_t cblocks = (k / kChunk + kQBlock - 1) / kQBlock;
+  return dim3((unsigned)(tiles * cblocks));
 }
 
 }  // namespace
 
 hipError_t launch_quantize_t2(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                               uint16_t* scales, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_t2_kernel, tile_grid(n, k), dim3(kBlock), 0, st, w, n, k, codes,
+  hipLaunchKernelGGL(quantize_t2_kernel, tile_grid(n, k), dim3(kQBlock), 0, st, w, n, k, codes,
                      scales);
   return hipGetLastError();
 }
