@@ -16,7 +16,9 @@
 // prepare launch, no workspace, no atomics and no zeroed y:
 //   * wave w takes K-range [512 w, 512 w + 512) (64 chunks of 8 weights);
 //     lane (rho = l % 16, q = l / 16) takes row rho of the tile and chunks
-//     q, q + 4, ..., q + 60 of that range (16 chunks, 4 groups);
+//     q, q + 4, ..., q + 60 of that range (16 chunks, 4 groups); with half
+//     tiles, lane (l % 8, l / 8) takes one of the 8 rows and chunks q,
+//     q + 8, ..., q + 56 (8 chunks);
 //   * every load of the lane is issued at once: one code dword per chunk
 //     (rows 4 (rho / 4) .. + 3 of the cell; ternary: pos and neg), one scale
 //     dword per group (rows rho & ~1, + 1), and, for b <= 2, x as 16-byte
@@ -27,8 +29,8 @@
 //     (+s or -s; ternary also 0) and v_dot2_f32_f16 adds (+-s) x for two
 //     weights at a time into an FP32 sum -- products of two FP16 numbers are
 //     exact in FP32;
-//   * the four quarter lanes of a row are summed across lanes, the waves'
-//     sums through LDS, and y is stored once.
+//   * the lanes of a row are summed across lanes, the waves' sums through
+//     LDS, and y is stored once.
 // The FFN variant (SILU) takes h = [gate | up] (FP32 [b][2k]) instead of x
 // and forms z = RNE_fp16(SiLU(gate) * up) itself: lane l of wave w forms
 // chunk 64 w + l into LDS, from where the lanes that need it read it.
