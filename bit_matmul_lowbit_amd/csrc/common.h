@@ -68,6 +68,18 @@ template <int P>
 constexpr uint32_t kPairShift = ((uint32_t)(14 - 2 * P) << 16) | (uint32_t)(15 - 2 * P);
 constexpr uint32_t kSignBits = 0x80008000u;
 
+// Bits 2P and 2P + 1 of byte J of w at bits 15 and 31 (the other bits are
+// left as they fall): the 16-bit half that holds byte J feeds both halves of
+// one packed shift (v_pk_lshlrev_b16 with op_sel), so the byte is not moved
+// first.
+template <int J, int P>
+__device__ __forceinline__ uint32_t byte_pair_bits(uint32_t w) {
+  const s16x2 a = __builtin_bit_cast(s16x2, w);
+  const s16x2 h = __builtin_shufflevector(a, a, J >> 1, J >> 1);
+  constexpr short lo = (short)(15 - 2 * P - 8 * (J & 1)), hi = (short)(14 - 2 * P - 8 * (J & 1));
+  return __builtin_bit_cast(uint32_t, (s16x2)(h << (s16x2){lo, hi}));
+}
+
 // SiLU(v) = v / (1 + e^-v) in FP32 with the device library's expf; for
 // v < -88 e^-v is infinite and the quotient is -0.
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }

@@ -14,23 +14,26 @@
 // (or, for a matrix with fewer tiles than twice the CUs, half a tile) over
 // the whole of K and writes its outputs with plain stores, so there is no
 // prepare launch, no workspace, no atomics and no zeroed y:
-//   * wave w takes K-range [512 w, 512 w + 512) (64 chunks of 8 weights);
-//     lane (rho = l % 16, q = l / 16) takes row rho of the tile and chunks
-//     q, q + 4, ..., q + 60 of that range (16 chunks, 4 groups); with half
-//     tiles, lane (l % 8, l / 8) takes one of the 8 rows and chunks q,
-//     q + 8, ..., q + 56 (8 chunks);
-//   * every load of the lane is issued at once: one code dword per chunk
-//     (rows 4 (rho / 4) .. + 3 of the cell; ternary: pos and neg), one scale
-//     dword per group (rows rho & ~1, + 1), and, for b <= 2, x as 16-byte
-//     FP16 vectors; for b >= 3 (k <= 4096) the work-group copies x into LDS
-//     once while those loads are in flight, and lanes read it from there;
-//   * the code byte of row rho goes to the low byte of both 16-bit halves
-//     (v_perm), a packed shift and v_bitop3 turn each bit pair into FP16
-//     (+s or -s; ternary also 0) and v_dot2_f32_f16 adds (+-s) x for two
-//     weights at a time into an FP32 sum -- products of two FP16 numbers are
-//     exact in FP32;
-//   * the lanes of a row are summed across lanes, the waves' sums through
-//     LDS, and y is stored once.
+//   * wave w takes K-range [512 w, 512 w + 512) (64 chunks of 8 weights).
+//     A code dword of a cell holds one byte of each of 4 rows, and a lane
+//     takes all 4: lane (q = l % 16, m = l / 16) takes rows 4m .. 4m + 3 of
+//     the tile and chunks q, q + 16, q + 32, q + 48 of the range (one per
+//     group); with half tiles, lane (l % 32, l / 32) takes 4 of the 8 rows
+//     and chunks q, q + 32.  The 16 (32) lanes of a row quad read 16 (32)
+//     adjacent cells;
+//   * loads go out in the order they are needed: first what the work-group
+//     stages in LDS (x for b >= 3, k <= 4096; h for the FFN variant), then,
+//     chunk by chunk, the code dword (ternary: pos and neg), the 4 rows'
+//     scales of the chunk's group (8 bytes) and, for b <= 2, x as a 16-byte
+//     FP16 vector.  Loads complete in order, so the staging waits for no
+//     code load and each chunk's arithmetic waits only for its own loads;
+//   * a packed shift fed the 16-bit half that holds a row's byte (op_sel, no
+//     byte moves) and v_bitop3 turn each bit pair into FP16 (+s or -s;
+//     ternary also 0) and v_dot2_f32_f16 adds (+-s) x for two weights at a
+//     time into an FP32 sum -- products of two FP16 numbers are exact in
+//     FP32;
+//   * the lanes of a row quad are summed on DPP (two transposed stages leave
+//     one row per lane), the waves' sums through LDS, and y is stored once.
 // The FFN variant (SILU) takes h = [gate | up] (FP32 [b][2k]) instead of x
 // and forms z = RNE_fp16(SiLU(gate) * up) itself: lane l of wave w forms
 // chunk 64 w + l into LDS, from where the lanes that need it read it.
@@ -40,7 +43,6 @@ namespace lowbit {
 namespace {
 
 constexpr int kWaveK = 512;           // weights of K per wave
-constexpr int kLaneChunks = 16;       // chunks per lane
 constexpr int kMaxWaves = 16;         // K <= 8192
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -64,6 +66,17 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int p) {
   return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w;
 }
 
+// v of the lane named by a DPP control (within rows of 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppRor8 = 0x128;        // lane i <- lane (i + 8) mod 16 (= i ^ 8)
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+
 // per-half arithmetic shift right by 15: 0xFFFF where bit 15 is set, else 0
 __device__ __forceinline__ uint32_t mask15(uint32_t d) {
   const s16x2 a = __builtin_bit_cast(s16x2, d);
@@ -78,15 +91,18 @@ constexpr int max_waves() { return B <= 2 ? kMaxWaves : kMaxKLds / kWaveK; }
 
 // RH = rows per work-group: 16 (a tile), or 8 (half a tile, for matrices
 // with fewer tiles than twice the CUs: twice the work-groups, each lane half
-// the chunks).  Lane (rho, q): row rho of the work-group's RH rows, chunks
-// q, q + QN, ... of the wave's range (QN = 64 / RH lanes per row).
+// the chunks).  A code dword of a cell holds 4 rows (one byte each), and a
+// lane takes all 4: lane (q, m) = (l % QN, l / QN) takes rows rq .. rq + 3
+// (rq = r0 + 4 m, m < RH / 4) of chunks q, q + QN, ... of the wave's range
+// (QN = 256 / RH chunk lanes per row quad, LC = 64 / QN chunks each).
 template <int FMT, int B, bool SILU, int RH>
 __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const void* __restrict__ xin, int64_t n, int64_t k, float* __restrict__ y) {
   constexpr int CB = Fmt<FMT>::cell_bytes;
-  constexpr int QN = 64 / RH;               // lanes per row
-  constexpr int LC = kLaneChunks * 4 / QN;  // chunks per lane
+  constexpr int MQ = RH / 4;                // row quads per work-group
+  constexpr int QN = 64 / MQ;               // chunk lanes per row quad
+  constexpr int LC = kWaveK / kChunk / QN;  // chunks per lane
   static_assert(RH == 16 || RH == 8, "a tile or half a tile per work-group");
   constexpr bool XLDS = !SILU && B >= 3;  // x staged in LDS
   __shared__ uint4 zbuf[SILU ? max_waves<B>() * 64 * B : 1];
@@ -97,7 +113,7 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
   const int nw = (int)(blockDim.x >> 6);
   const int64_t tile = RH == 16 ? blockIdx.x : blockIdx.x >> 1;
   const int r0 = RH == 16 ? 0 : (int)(blockIdx.x & 1) * 8;  // first row in the tile
-  const int rho = r0 + (lane % RH), q = lane / RH;             // row in the tile, chunk lane
+  const int q = lane % QN, rq = r0 + 4 * (lane / QN);       // chunk lane, first of 4 rows
   const int64_t nch = k / kChunk;
   const int64_t G = k / kGroup;
   const int c0 = wave * (kWaveK / kChunk);  // first chunk of the wave
@@ -107,68 +123,88 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + tile * G * 16, G * 32);
   constexpr uint32_t kNoLoad = 0x80000000u;
 
-  // chunk c0 + q + QN i lies in group c0 / 16 + (q + QN i) / 16 = c0 / 16 + i / (16 / QN)
-  constexpr int IPG = 16 / QN;  // a lane's chunks per group
-  uint32_t cw[LC], nwd[FMT == 2 ? LC : 1], sw[LC / IPG];
-#pragma unroll
-  for (int i = 0; i < LC; ++i) {
-    const uint32_t off = (uint32_t)((c0 + q + QN * i) * CB + (rho & 12));
-    cw[i] = dload(rc, off);
-    if constexpr (FMT == 2) nwd[i] = dload(rc, off + 16);
-  }
-#pragma unroll
-  for (int j = 0; j < LC / IPG; ++j)
-    sw[j] = dload(rs, (uint32_t)(((c0 / 16 + j) * 16 + (rho & 14)) * 2));
-
-  uint4 xv[SILU || XLDS ? 1 : LC][B];
+  // Loads, in the order the work-group needs them: first what is staged in
+  // LDS (x for b >= 3, h for the FFN variant: thread t takes chunk c0 + lane
+  // of every batch row), then the lane's chunks one by one (code dword(s),
+  // the 4 rows' scales of the chunk's group -- 8 contiguous bytes -- and,
+  // for b <= 2, x).  Loads complete in order, so staging waits for no code
+  // load, and the contraction of chunk i waits only for the loads up to it.
   const int pitch = nw * 64;  // chunks per x row in LDS: zeros past k
+  const int64_t cs = c0 + lane;  // chunk staged by this thread
+  uint4 xs[XLDS ? B : 1];
+  float4 hs[SILU ? B : 1][4];
   if constexpr (XLDS) {
-    // x [B][k] FP16 into LDS, 16 bytes per thread and round
-    const uint4* x4 = static_cast<const uint4*>(xin);
-    for (int v = threadIdx.x; v < B * pitch; v += blockDim.x) {
-      const int bi = v / pitch, c = v - bi * pitch;
-      xbuf[v] = c < nch ? x4[bi * nch + c] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
-  } else if constexpr (SILU) {
-    // z of chunk c0 + lane, all batch rows, into LDS (zeros past k)
-    const float* h = static_cast<const float*>(xin);
-    const int64_t c = c0 + lane;
-#pragma unroll
-    for (int bi = 0; bi < B; ++bi) {
-      uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      if (c < nch) {
-        const float4* g4 = reinterpret_cast<const float4*>(h + bi * 2 * k + c * 8);
-        const float4* u4 = reinterpret_cast<const float4*>(h + bi * 2 * k + k + c * 8);
-        const float4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
-        const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-        const float uv[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-        z = silu_mul8(gv, uv);
-      }
-      zbuf[(wave * 64 + lane) * B + bi] = z;
-    }
-    __syncthreads();
-  } else {
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xin, B * k * 2);
 #pragma unroll
-    for (int i = 0; i < LC; ++i) {
-      const int c = c0 + q + QN * i;
+    for (int bi = 0; bi < B; ++bi)
+      xs[bi] = qload(rx, cs < nch ? (uint32_t)((bi * k + cs * 8) * 2) : kNoLoad);
+  } else if constexpr (SILU) {
+    const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(xin, B * 2 * k * 4);
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      const uint32_t go = cs < nch ? (uint32_t)((bi * 2 * k + cs * 8) * 4) : kNoLoad;
+      const uint32_t uo = cs < nch ? go + (uint32_t)(k * 4) : kNoLoad;
+      const uint4 a = qload(rh, go), b2 = qload(rh, go + (cs < nch ? 16u : 0u));
+      const uint4 c = qload(rh, uo), d = qload(rh, uo + (cs < nch ? 16u : 0u));
+      hs[bi][0] = __builtin_bit_cast(float4, a);
+      hs[bi][1] = __builtin_bit_cast(float4, b2);
+      hs[bi][2] = __builtin_bit_cast(float4, c);
+      hs[bi][3] = __builtin_bit_cast(float4, d);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint32_t cw[LC], nwd[FMT == 2 ? LC : 1];
+  uint2 sw[LC];
+  uint4 xv[SILU || XLDS ? 1 : LC][B];
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xin, B * k * 2);
+#pragma unroll
+  for (int i = 0; i < LC; ++i) {
+    const int c = c0 + q + QN * i;
+    const uint32_t off = (uint32_t)(c * CB + rq);
+    cw[i] = dload(rc, off);
+    if constexpr (FMT == 2) nwd[i] = dload(rc, off + 16);
+    // chunk c lies in group c / 16; the 4 rows' scales of it are 8 bytes
+    const auto s2 = __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)(((c >> 4) * 16 + rq) * 2), 0, 0);
+    sw[i] = make_uint2(s2[0], s2[1]);
+    if constexpr (!SILU && !XLDS) {
 #pragma unroll
       for (int bi = 0; bi < B; ++bi)
         xv[i][bi] = qload(rx, c < nch ? (uint32_t)((bi * k + c * 8) * 2) : kNoLoad);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the chunks' loads in this order
   }
 
-  // byte rho & 3 of a code dword in the low byte of both halves; the scale
-  // of row rho in both halves
-  const uint32_t bsel = 0x0C000C00u | ((uint32_t)(rho & 3) << 16) | (uint32_t)(rho & 3);
-  const uint32_t ssel = (rho & 1) ? 0x03020302u : 0x01000100u;
-  float acc[B];
+  if constexpr (XLDS) {
+    // x [B][k] FP16 into LDS (zeros past k)
 #pragma unroll
-  for (int bi = 0; bi < B; ++bi) acc[bi] = 0.0f;
+    for (int bi = 0; bi < B; ++bi) xbuf[bi * pitch + cs] = xs[bi];
+  } else if constexpr (SILU) {
+    // z of chunk c0 + lane, all batch rows, into LDS (zeros past k: h reads 0)
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      const float gv[8] = {hs[bi][0].x, hs[bi][0].y, hs[bi][0].z, hs[bi][0].w,
+                           hs[bi][1].x, hs[bi][1].y, hs[bi][1].z, hs[bi][1].w};
+      const float uv[8] = {hs[bi][2].x, hs[bi][2].y, hs[bi][2].z, hs[bi][2].w,
+                           hs[bi][3].x, hs[bi][3].y, hs[bi][3].z, hs[bi][3].w};
+      zbuf[(wave * 64 + lane) * B + bi] = silu_mul8(gv, uv);
+    }
+  }
+  if constexpr (XLDS || SILU) {
+    // the LDS stores done (the staging loads are, being the oldest); the
+    // code loads stay in flight across the barrier
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(63));
+    stage_barrier();
+  }
+
+  // acc[r][bi]: row rq + r, batch row bi
+  float acc[4][B];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) acc[r][bi] = 0.0f;
 #pragma unroll
   for (int i = 0; i < LC; ++i) {
-    const uint32_t ss = __builtin_amdgcn_perm(sw[i / IPG], sw[i / IPG], ssel);
     uint4 xi[B];
 #pragma unroll
     for (int bi = 0; bi < B; ++bi) {
@@ -180,37 +216,49 @@ __global__ __launch_bounds__(64 * max_waves<B>()) void gemv_direct_kernel(
         xi[bi] = xv[i][bi];
       }
     }
-    if constexpr (FMT == 1) {
-      const uint32_t d = __builtin_amdgcn_perm(cw[i], cw[i], bsel);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t sh = ((uint32_t)(14 - 2 * p) << 16) | (uint32_t)(15 - 2 * p);
-        const uint32_t a = ss ^ (~pk_shl(d, sh) & kSignBits);
-#pragma unroll
-        for (int bi = 0; bi < B; ++bi) acc[bi] = dot2(a, word(xi[bi], p), acc[bi]);
-      }
-    } else {
-      const uint32_t dq = __builtin_amdgcn_perm(nwd[i], nwd[i], bsel);        // neg
-      const uint32_t dn = __builtin_amdgcn_perm(cw[i] ^ nwd[i], cw[i] ^ nwd[i], bsel);  // nonzero
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t sh = ((uint32_t)(14 - 2 * p) << 16) | (uint32_t)(15 - 2 * p);
-        const uint32_t a = (ss ^ (pk_shl(dq, sh) & kSignBits)) & mask15(pk_shl(dn, sh));
-#pragma unroll
-        for (int bi = 0; bi < B; ++bi) acc[bi] = dot2(a, word(xi[bi], p), acc[bi]);
-      }
-    }
+    const uint32_t dn = FMT == 2 ? cw[i] ^ nwd[i] : 0u;  // ternary: nonzero
+    // row r: code byte r, scale half r of the group's 4 scales (both halves)
+#define LOWBIT_DROW(R)                                                                      \
+  {                                                                                         \
+    const uint32_t sv = (R) < 2 ? sw[i].x : sw[i].y;                                        \
+    const uint32_t ss = __builtin_amdgcn_perm(sv, sv, ((R) & 1) ? 0x03020302u : 0x01000100u); \
+    LOWBIT_DPAIR(R, 0) LOWBIT_DPAIR(R, 1) LOWBIT_DPAIR(R, 2) LOWBIT_DPAIR(R, 3)             \
   }
-  // the QN lanes of a row, then the waves
+#define LOWBIT_DPAIR(R, P)                                                                  \
+  {                                                                                         \
+    uint32_t a;                                                                             \
+    if constexpr (FMT == 1)                                                                 \
+      a = ss ^ (~byte_pair_bits<R, P>(cw[i]) & kSignBits);                                  \
+    else                                                                                    \
+      a = (ss ^ (byte_pair_bits<R, P>(nwd[i]) & kSignBits)) & mask15(byte_pair_bits<R, P>(dn)); \
+    _Pragma("unroll") for (int bi = 0; bi < B; ++bi) acc[R][bi] = dot2(a, word(xi[bi], P), acc[R][bi]); \
+  }
+    LOWBIT_DROW(0) LOWBIT_DROW(1) LOWBIT_DROW(2) LOWBIT_DROW(3)
+#undef LOWBIT_DPAIR
+#undef LOWBIT_DROW
+  }
+  // Sum over the QN lanes of a row quad (lane bits 0 .. log2 QN - 1), on
+  // DPP within 16-lane rows.  Two transposed stages leave each lane one of
+  // the 4 rows, r = 2 bit3 + bit2: on bit 3 with lane i ^ 8, on bit 2 with
+  // the half-row mirror 7 - i (which also flips bits 1 and 0: harmless, the
+  // butterflies on those bits follow); bit 4 (QN = 32) by a lane shuffle.
 #pragma unroll
   for (int bi = 0; bi < B; ++bi) {
-    if constexpr (QN == 8) acc[bi] += __shfl_xor(acc[bi], 8);
-    acc[bi] += __shfl_xor(acc[bi], 16);
-    acc[bi] += __shfl_xor(acc[bi], 32);
+    const bool h3 = (q >> 3) & 1, h2 = (q >> 2) & 1;
+    const float k0 = h3 ? acc[2][bi] : acc[0][bi], s0 = h3 ? acc[0][bi] : acc[2][bi];
+    const float k1 = h3 ? acc[3][bi] : acc[1][bi], s1 = h3 ? acc[1][bi] : acc[3][bi];
+    const float v0 = k0 + dpp_f32<kDppRor8>(s0);
+    const float v1 = k1 + dpp_f32<kDppRor8>(s1);
+    float v = (h2 ? v1 : v0) + dpp_f32<kDppHalfMirror>(h2 ? v0 : v1);
+    v += dpp_f32<kDppQuadXor2>(v);
+    v += dpp_f32<kDppQuadXor1>(v);
+    if constexpr (QN == 32) v += __shfl_xor(v, 16);
+    acc[0][bi] = v;
   }
-  if (q == 0) {
+  if ((q & ~12) == 0) {
+    const int row = rq + 2 * ((q >> 3) & 1) + ((q >> 2) & 1);
 #pragma unroll
-    for (int bi = 0; bi < B; ++bi) red[wave * RH * B + bi * RH + (rho - r0)] = acc[bi];
+    for (int bi = 0; bi < B; ++bi) red[wave * RH * B + bi * RH + (row - r0)] = acc[0][bi];
   }
   __syncthreads();
   // RH B outputs; a work-group of one wave (k <= 512) may have fewer threads
