@@ -9,8 +9,8 @@ Tolerances, from the arithmetic:
   (a few FP32 ulps, well under 1e-6 relative) and rounds once to FP16: its
   output must be the FP16 rounding of the exact double value, except where
   that value lies within 1e-6 (relative) of an FP16 rounding boundary,
-  where either neighbour is accepted; a value that rounds to zero may be
-  either zero;
+  where either neighbour is accepted; a value that rounds to zero keeps the
+  sign of the product (checked on its own at the edge values);
 * the whole chain adds the FP32 GEMV error to h, so a z value whose exact
   double lies near an FP16 rounding boundary can round one FP16 ulp the
   other way.  Each such flip moves an output by |w| * ulp(z) and the flips
