@@ -60,6 +60,18 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kSteps = 4;            // 32-k MFMA steps per 128-weight group
 constexpr int kXStep = 64 * 16;      // bytes of A operand per step (64 lanes x 16 B)
 constexpr int kRedPitch = 260;       // LDS pitch per batch row (256 rows + pad)
+
+// Persistent kernel's item-end buffer: float4 (batch rows 4q .. 4q + 3) of
+// wave w, lane quarter q < 2, row rho of tile `tile` of the item's block.
+// The 16 tiles of one (w, q, rho) are contiguous (a wave's 16-byte stores
+// fill 256 contiguous bytes per quarter), and rows rho are 68 floats apart
+// (272 bytes, 16 mod 256), so the 16 rows read by a 16-lane phase of the
+// summing threads fall in different 16-byte bank groups.
+constexpr int kRedRowF4 = 17;  // float4 per (w, q, rho): 16 tiles + pad
+constexpr int kRedFloats = kWaves * 2 * 16 * kRedRowF4 * 4;
+__device__ __forceinline__ int red_at(int w, int q, int rho, int tile) {
+  return ((w * 2 + q) * 16 + rho) * kRedRowF4 + tile;
+}
 constexpr uint32_t kNoLoad = 0x80000000u;  // lane offset past any resource: zeros
 
 // byte offset of a lane's code cell i of a group, from the lane's quarter base
@@ -207,7 +219,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint4* __restrict__ xw, float* __restrict__ y, int64_t n, int64_t k, int b,
     int64_t ntiles, int kpieces, int gpp, int64_t nitems) {
-  __shared__ float red[kWaves * 16 * kRedPitch];
+  // item-end reduction buffers, two so that one barrier per item suffices
+  // (the next item writes the other buffer; a wave can only reach the item
+  // after that once every wave has passed the next barrier, i.e. finished
+  // reading this one)
+  __shared__ float4 red4[2 * kRedFloats / 4];
   constexpr int D = 2;  // groups of loads in flight per wave, plus the one in use
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -254,6 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   GroupRegs<FMT> ring[D];
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) load(ring[i], i);
+  int rb = 0;  // reduction buffer of the next item end
   for (int64_t sl = 0; sl < total; sl += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
@@ -265,31 +282,37 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
       const int64_t cur = sl + u;
       if (cur < total && (cur + 1) % per == 0) {
-        // end of an item: partial sums of the waves -> LDS -> y
+        // end of an item: partial sums of the waves -> LDS -> y.  Batch
+        // rows 0..7 (b <= 8) sit in lanes q = 0, 1: each writes its 4 rows
+        // of acc[r] as one 16-byte store, red_at(w, q, r, tile) + v
         const int64_t item = blockIdx.x + (cur / per) * (int64_t)gridDim.x;
         const int64_t T0 = (item / kpieces) * 16;
+        float4* red = red4 + rb * (kRedFloats / 4);
+        if (q < 2) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            red[(wave * 16 + 4 * q + v) * kRedPitch + r * 16 + tl] = acc[r][v];
-            acc[r][v] = 0.0f;
-          }
+          for (int r = 0; r < 16; ++r)
+            red[red_at(wave, q, r, tl)] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
         __syncthreads();
-        // thread t: row T0 * 16 + t (t = 16 * tile + rho)
+        // thread t: row T0 * 16 + t (t = 16 * tile + rho), batch rows 0..7
         const int t = threadIdx.x;
         const int64_t row = T0 * 16 + t;
-        const int rr = (t & 15) * 16 + (t >> 4);
-        if (row < n) {
-          for (int i = 0; i < b; ++i) {
-            float sum = 0.0f;
+        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) sum += red[(w * 16 + i) * kRedPitch + rr];
-            atomicAdd(y + i * n + row, sum);
-          }
+        for (int w = 0; w < kWaves; ++w) {
+          const float4 a = red[red_at(w, 0, t & 15, t >> 4)], c = red[red_at(w, 1, t & 15, t >> 4)];
+          s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
+          s1.x += c.x; s1.y += c.y; s1.z += c.z; s1.w += c.w;
         }
-        __syncthreads();
+        if (row < n) {
+          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (i < b) atomicAdd(y + i * n + row, sv[i]);
+        }
+        rb ^= 1;
       }
     }
   }
