@@ -455,12 +455,15 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scale
   // 4 * per groups (per groups for each wave): per is chosen for about four
   // items per work-group, but at least two groups per wave (each item ends
   // with an LDS reduction and atomics) and no more than K holds.  The grid
-  // is then sized so that every work-group gets the same number of items;
-  // a matrix with few items (at most two per resident slot) gets one
-  // work-group per item instead, as many loads in flight as possible.  A
-  // matrix whose two-group items would not even give every CU one takes a
-  // single group per wave (twice the items): 6144x2048 ternary at b = 3..8
-  // runs 12.2 -> 11.1 us, while larger matrices lose with it.
+  // is two work-groups per CU (fewer only if there are fewer items), all
+  // resident at once, so a work-group with a second item has its loads in
+  // flight while it finishes the first; one work-group per item, with the
+  // items past the resident ones launched as a second round, ran the 27B
+  // gate+up (680 items) at b = 5 / 8 in 15.0-15.5 / 15.5-16.0 us instead
+  // of 14.3 / 14.7 us.  A matrix whose two-group items would not even give
+  // every CU one takes a single group per wave (twice the items):
+  // 6144x2048 ternary at b = 3..8 runs 12.2 -> 11.1 us, while larger
+  // matrices lose with it (27B gate+up at b = 5: 19 us).
   const int64_t nwg_max = 2 * (int64_t)cus;
   int64_t per = (int64_t)G * nblocks / (4 * kWaves * nwg_max);
   const int64_t per_max = (G + kWaves - 1) / kWaves;
@@ -469,8 +472,7 @@ hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scale
   const int gpp = (int)(kWaves * per);
   const int64_t kp = (G + gpp - 1) / gpp;
   const int64_t nitems = nblocks * kp;
-  const int64_t rounds = (nitems + nwg_max - 1) / nwg_max;
-  const int64_t nwg = nitems <= 2 * nwg_max ? nitems : (nitems + rounds - 1) / rounds;
+  const int64_t nwg = nitems < nwg_max ? nitems : nwg_max;
   const uint4* xw = static_cast<const uint4*>(ws);
   // no more items than CUs: one item per work-group, x from LDS (ternary
   // 6144x2048 and 2048x6144 at b = 5: 11.1 -> 9.0 us; the 27B-class
