@@ -574,6 +574,31 @@ def ceilings():
                                  "tflops": rounded(stats(res[best]), 1),
                                  "frac_of_bf16_peak": round(float(sorted(res[best])[2]) / BF16_PEAK_TFLOPS, 4)}
     del msink
+
+    # the matrix-core GEMV's per-row work (512 weights: byte expansion +
+    # one 16x16x32 MFMA) on register data, per SIMD, at one and two waves
+    # per SIMD (the kernel runs two); its floor for the 27B matrices
+    esink = torch.zeros(2 * cus * 256, dtype=torch.float32, device="cuda")
+    eres = {}
+    for mode, name in ((0, "expansion+mfma"), (1, "mfma")):
+        for bpc in (1, 2):
+            lowbit.lowbit_probe_expand_mfma(mode, 100, bpc, esink)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                a.record()
+                steps = lowbit.lowbit_probe_expand_mfma(mode, 4000, bpc, esink)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e6 / steps)
+            eres[f"{name},{bpc}/simd"] = round(float(np.median(ts)), 2)
+    step_ns = eres["expansion+mfma,2/simd"]
+    out["gemv_mfma_row_step"] = {
+        "ns_per_row_step_per_simd": eres, "weights_per_row_step": 512,
+        "floor_us_at_2_waves_per_simd": {
+            f"q1_{n}x{k}": round(n * k / 512 / (4 * cus) * step_ns / 1e3, 2)
+            for n, k in ((34816, 5120), (5120, 17408))}}
+    del esink
     torch.cuda.empty_cache()
     return out
 

@@ -147,6 +147,10 @@ hipError_t launch_gemv_mfma_prepare(int64_t n, int64_t k, const uint16_t* x, int
 hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                             int64_t k, int64_t b, float* y, const void* ws, int cus,
                             hipStream_t st);
+// ceiling probe: the matrix-core GEMV's per-row expansion and MFMA on
+// register data (mode 0: expansion + MFMA, 1: the MFMA alone), `blocks` work-groups
+// of 256 threads
+hipError_t launch_probe_expand_mfma(int mode, int iters, int blocks, float* sink, hipStream_t st);
 size_t gemv_workspace_bytes(int64_t k, int64_t b);
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st);

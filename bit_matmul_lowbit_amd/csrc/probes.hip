@@ -1,5 +1,7 @@
-// Ceiling probes (include/lowbit_probes.h): a streaming read and a
-// matrix-core loop, each doing nothing but the one thing it measures.
+// Ceiling probes (include/lowbit_probes.h): a streaming read, a
+// matrix-core loop and an LDS read loop, each doing nothing but the one
+// thing it measures; the probe of the matrix-core GEMV's per-row work sits
+// next to that kernel (gemv_mfma.hip), whose expansion it runs.
 // Context for the roofline of the library's kernels; not on the y = W.x path.
 #include "../../include/lowbit.h"
 #include "../../include/lowbit_probes.h"
@@ -139,6 +141,18 @@ int lowbit_probe_mfma_bf16(int iters, int blocks_per_cu, float* sink, hipStream_
   hipLaunchKernelGGL(lowbit::probe_mfma_bf16_kernel, dim3(blocks), dim3(256), 0, stream, iters,
                      sink);
   return hipGetLastError() == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+int lowbit_probe_expand_mfma(int mode, int iters, int blocks_per_cu, float* sink,
+                             hipStream_t stream) {
+  if (!sink || mode < 0 || mode > 1 || blocks_per_cu < 1 || blocks_per_cu > 4 || iters < 1 ||
+      iters > (1 << 24))
+    return LOWBIT_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(sink) & 3u) return LOWBIT_ERR_ALIGN;
+  const int blocks = blocks_per_cu * lowbit::device_cu_count();
+  return lowbit::launch_probe_expand_mfma(mode, iters, blocks, sink, stream) == hipSuccess
+             ? LOWBIT_OK
+             : LOWBIT_ERR_HIP;
 }
 
 }  // extern "C"

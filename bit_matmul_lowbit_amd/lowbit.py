@@ -33,7 +33,7 @@ SYMBOLS = [
 
 # ceiling probes (include/lowbit_probes.h): context for the roofline only
 PROBE_SYMBOLS = ["lowbit_probe_stream_read", "lowbit_probe_mfma_bf16", "lowbit_probe_lds_read",
-                 "lowbit_probe_cu_count"]
+                 "lowbit_probe_expand_mfma", "lowbit_probe_cu_count"]
 
 
 class LowbitError(RuntimeError):
@@ -93,6 +93,7 @@ def load() -> ctypes.CDLL:
         "lowbit_probe_stream_read": ([p, sz, i, i, p, p], i),
         "lowbit_probe_mfma_bf16": ([i, i, p, p], i),
         "lowbit_probe_lds_read": ([i, i, p, p], i),
+        "lowbit_probe_expand_mfma": ([i, i, i, p, p], i),
         "lowbit_probe_cu_count": ([], i),
     }
     for name, (args, res) in sig.items():
@@ -575,3 +576,16 @@ def lowbit_probe_lds_read(iters: int, blocks_per_cu: int, sink, stream=None):
                                         _dev(sink, (torch.int32, torch.uint32), "sink"),
                                         _stream(stream)), "lowbit_probe_lds_read")
     return blocks * 256 * iters * 8 * 16
+
+
+def lowbit_probe_expand_mfma(mode: int, iters: int, blocks_per_cu: int, sink, stream=None):
+    """Probe of the matrix-core GEMV's per-row work (mode 0: expansion +
+    MFMA, 1: the MFMA alone); returns the row steps each SIMD runs."""
+    import torch
+
+    blocks = blocks_per_cu * lowbit_probe_cu_count()
+    _need_numel(sink, blocks * 256, "sink")
+    _check(load().lowbit_probe_expand_mfma(mode, iters, blocks_per_cu,
+                                           _dev(sink, (torch.float32,), "sink"), _stream(stream)),
+           "lowbit_probe_expand_mfma")
+    return blocks_per_cu * iters * 16

@@ -1,13 +1,17 @@
 /*
  * lowbit_probes.h -- measured ceilings for the roofline of liblowbit.so's
- * kernels on this GPU.  Context only: neither probe is part of the y = W.x
+ * kernels on this GPU.  Context only: no probe is part of the y = W.x
  * path; bench.py times them next to the kernels, so that a kernel's rate can
  * be set against what the machine delivers to a kernel that does nothing
  * else, as well as against the vendor's peak figures.
  *
  * [P2] 7minutos.es, "PrismML lanza Bonsai 27B ...", "Rendimiento y
  * decodificacion especulativa DSpark": decode is bound by memory bandwidth,
- * prefill by compute -- hence one probe of each.
+ * prefill by compute -- hence a streaming-read and a matrix-core probe (and
+ * an LDS probe for the table GEMV).  The same section's speculative verify
+ * runs decode at a small batch, where the matrix-core GEMV is bound by its
+ * own per-weight arithmetic rather than by memory: a fourth probe runs that
+ * arithmetic alone.
  *
  * Conventions as in lowbit.h: device pointers, host-side validation, the
  * kernels are enqueued on `stream` and the call returns without waiting.
@@ -51,6 +55,21 @@ int lowbit_probe_mfma_bf16(int iters, int blocks_per_cu, float* sink, hipStream_
  * a fixed constant.  Bytes read = blocks * 256 * iters * 8 * 16.
  * 1 <= blocks_per_cu <= 4, 1 <= iters <= 2^24.  Returns a lowbit_status. */
 int lowbit_probe_lds_read(int iters, int blocks_per_cu, uint32_t* sink, hipStream_t stream);
+
+/* The matrix-core GEMV's per-row work (lowbit_gemv at b >= 3): one code
+ * byte expanded to eight FP16 operands +s / -s (a byte move, then four
+ * packed shifts and four v_bitop3) and one v_mfma_f32_16x16x32_f16 -- 512
+ * weights -- on register data, as the kernel issues them.  Every wave of
+ * blocks_per_cu * (compute units) work-groups of 256 threads (so
+ * blocks_per_cu waves per SIMD) runs iters x 16 such row steps.  mode 0:
+ * expansion + MFMA, 1: the MFMA alone; `sink`
+ * ([blocks * 256] float, device) is written only if a result equals a
+ * fixed constant.  Time / (blocks_per_cu * iters * 16) is the time per row
+ * step on one SIMD: with mode 0 and the kernel's two waves per SIMD, the
+ * floor that this arithmetic puts under the kernel.  1 <= blocks_per_cu
+ * <= 4, 1 <= iters <= 2^24.  Returns a lowbit_status. */
+int lowbit_probe_expand_mfma(int mode, int iters, int blocks_per_cu, float* sink,
+                             hipStream_t stream);
 
 /* Compute units of the current device, as the probes and the kernels'
  * launchers count them (256 if the query fails). */
