@@ -37,12 +37,54 @@ __device__ __forceinline__ bool twice_gt(uint32_t m, uint32_t S) {
   return d > S;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// max |w| pattern over the 8 FP16 values of a chunk (4 words)
+__device__ __forceinline__ uint32_t chunk_max_mag(const uint32_t (&hw)[4]) {
+  u16x2 m = as_u16x2(hw[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int p = 1; p < 4; ++p) m = __builtin_elementwise_max(m, as_u16x2(hw[p] & 0x7FFF7FFFu));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// The pos and neg bytes of a chunk whose group scale pattern S is finite
+// (S < 0x7C00; S is the largest |w| of the group, so every |w| here is
+// finite too).  Two weights at a time: 2|w| as a pattern is m + min(m,
+// 0x400) (a subnormal doubles its fraction, a normal value adds one to its
+// exponent; at most 0x7FFF), and 2|w| > s is the sign bit of the wrapping
+// 16-bit difference S - 2|w| (both below 0x8000).  Bit 15 / 31 of word p
+// then holds weight 2p / 2p + 1; the four words' bits are gathered into a
+// byte with shifts and a bitwise select.
+__device__ __forceinline__ void chunk_trits_finite(const uint32_t (&hw)[4], uint32_t S,
+                                                   uint32_t& pb, uint32_t& nb) {
+  const u16x2 SS = {(unsigned short)S, (unsigned short)S};
+  uint32_t pos[4], neg[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const u16x2 m = as_u16x2(hw[p] & 0x7FFF7FFFu);
+    const u16x2 d = m + __builtin_elementwise_min(m, (u16x2){0x0400, 0x0400});
+    const uint32_t gt = as_u32(SS - d);  // bit 15 / 31: 2|w| > s
+    pos[p] = gt & ~hw[p] & 0x80008000u;
+    neg[p] = gt & hw[p] & 0x80008000u;
+  }
+  // weight 2p at bit 2p, weight 2p + 1 at bit 16 + 2p, then bit 2p + 1
+  const uint32_t dp = (pos[0] >> 15) | (pos[1] >> 13) | (pos[2] >> 11) | (pos[3] >> 9);
+  const uint32_t dn = (neg[0] >> 15) | (neg[1] >> 13) | (neg[2] >> 11) | (neg[3] >> 9);
+  pb = (dp & 0x55u) | ((dp >> 15) & 0xAAu);
+  nb = (dn & 0x55u) | ((dn >> 15) & 0xAAu);
+}
+
 // One lane per 8-weight chunk c of one 16-row tile, as the 1-bit quantiser.
 // A (rolled) loop over four blocks of four rows: load them, reduce their
 // group maxima over the 16 lanes of the group (two 16-bit maxima per
 // shuffle), decide their 32 weights, and shift the block's pos and neg code
 // words into place.  Only one block is live at a time, so the kernel keeps
-// enough waves in flight to stream at HBM speed.
+// enough waves in flight to stream at HBM speed (unrolling the loop so that
+// all four blocks' loads go out at once measured slower).  Groups with a
+// finite scale -- all but those holding an infinity or a NaN -- are decided
+// two weights at a time (chunk_trits_finite).
 __global__ __launch_bounds__(kQBlock) void quantize_t2_kernel(const uint16_t* __restrict__ w,
                                                               int64_t n, int64_t k,
                                                               uint8_t* __restrict__ codes,
@@ -72,11 +114,7 @@ __global__ __launch_bounds__(kQBlock) void quantize_t2_kernel(const uint16_t* __
       uint32_t mags = 0u;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        uint32_t mx = 0u;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j)
-          mx = max(mx, (hw[2 * pr + u][j >> 1] >> ((j & 1) * 16)) & 0x7FFFu);
-        mags |= mx << (16 * u);
+        mags |= chunk_max_mag(hw[2 * pr + u]) << (16 * u);
       }
 #pragma unroll
       for (int d = 8; d >= 1; d >>= 1)
@@ -86,13 +124,18 @@ __global__ __launch_bounds__(kQBlock) void quantize_t2_kernel(const uint16_t* __
       for (int u = 0; u < 2; ++u) {
         const uint32_t S = (mags >> (16 * u)) & 0xFFFFu;
         uint32_t pb = 0u, nb = 0u;
+        if (S < 0x7C00u) {
+          chunk_trits_finite(hw[2 * pr + u], S, pb, nb);
+        } else {
+          // a group holding an infinity or a NaN: weight by weight
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const uint32_t h = (hw[2 * pr + u][j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-          const uint32_t nz = twice_gt(h & 0x7FFFu, S) ? 1u : 0u;
-          const uint32_t sgn = h >> 15;
-          pb |= (nz & (sgn ^ 1u)) << j;
-          nb |= (nz & sgn) << j;
+          for (int j = 0; j < kChunk; ++j) {
+            const uint32_t h = (hw[2 * pr + u][j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+            const uint32_t nz = twice_gt(h & 0x7FFFu, S) ? 1u : 0u;
+            const uint32_t sgn = h >> 15;
+            pb |= (nz & (sgn ^ 1u)) << j;
+            nb |= (nz & sgn) << j;
+          }
         }
         pw |= pb << ((2 * pr + u) * 8);
         nw |= nb << ((2 * pr + u) * 8);
