@@ -26,12 +26,34 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return lo | (hi << 16);
 }
 
-// FP16 pattern -> Q1 bit: 1 iff the IEEE comparison w >= 0 holds.
-// +0 and -0 give 1; negative values, -inf and every NaN give 0.  Works on
-// the bit pattern, so subnormals are never flushed.
-__device__ __forceinline__ uint32_t q1_bit(uint32_t h) {
-  const uint32_t mag = h & 0x7FFFu;
-  return (h & 0x8000u) ? (mag == 0u) : (mag <= 0x7C00u);
+// FP16 pattern -> Q1 bit: 1 iff the IEEE comparison w >= 0 holds, i.e.
+// with m = |w| pattern: sign clear and m <= 0x7C00 (not a NaN), or sign set
+// and m == 0.  +0 and -0 give 1; negative values, -inf and every NaN give 0.
+// Works on the bit pattern, so subnormals are never flushed.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// The code byte (bit j = the bit of value j) and the max |w| pattern of one
+// chunk (4 words, two FP16 values each), two values at a time with packed
+// 16-bit operations: with m = |w| pattern, 0x7C00 - m wraps (bit 15 set)
+// iff m > 0x7C00 (a NaN), and m - 1 wraps iff m == 0, so bit 15 / 31 of
+// sign ? (m - 1) : ~(0x7C00 - m) is the IEEE w >= 0 of each value.  The
+// four words' bits are gathered into the byte with shifts and a select.
+__device__ __forceinline__ void q1_chunk(const uint32_t (&words)[4], uint32_t& byte,
+                                         uint32_t& mx) {
+  uint32_t keep[4];
+  u16x2 mm = {0, 0};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const u16x2 m = __builtin_bit_cast(u16x2, words[p] & 0x7FFF7FFFu);
+    mm = __builtin_elementwise_max(mm, m);
+    const uint32_t nan_hi = __builtin_bit_cast(uint32_t, (u16x2){0x7C00, 0x7C00} - m);
+    const uint32_t zero_hi = __builtin_bit_cast(uint32_t, m - (u16x2){1, 1});
+    keep[p] = ((words[p] & zero_hi) | (~words[p] & ~nan_hi)) & 0x80008000u;
+  }
+  mx = max((uint32_t)mm.x, (uint32_t)mm.y);
+  // value 2p at bit 2p, value 2p + 1 at bit 16 + 2p, then bit 2p + 1
+  const uint32_t d = (keep[0] >> 15) | (keep[1] >> 13) | (keep[2] >> 11) | (keep[3] >> 9);
+  byte = (d & 0x55u) | ((d >> 15) & 0xAAu);
 }
 
 __global__ __launch_bounds__(kBlock) void quantize_q1_kernel(
@@ -54,12 +76,7 @@ __global__ __launch_bounds__(kBlock) void quantize_q1_kernel(
     if (row < n) {
       const uint4 v = *reinterpret_cast<const uint4*>(w + row * k + c * kChunk);
       const uint32_t words[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        const uint32_t h = (words[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        byte |= q1_bit(h) << j;
-        mx = max(mx, h & 0x7FFFu);
-      }
+      q1_chunk(words, byte, mx);
     }
     bytes[r >> 2] |= byte << ((r & 3) * 8);
     if (r & 1) mags[r >> 1] |= mx << 16;
