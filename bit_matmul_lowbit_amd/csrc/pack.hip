@@ -103,6 +103,28 @@ __global__ __launch_bounds__(kBlock) void quantize_q1_kernel(
   scales[(tile * groups + g) * kTileRows + j] = (uint16_t)mag;  // pad rows get 0
 }
 
+// Bit 7 of each byte of x0 (weights 0..3) and x1 (weights 4..7) gathered
+// into bits 0..7: after d = x0 >> 7 | x1 >> 3 the weights sit at bits
+// 0, 8, 16, 24 (0..3) and 4, 12, 20, 28 (4..7); folding by 7 and then by
+// 14 bits brings 8, 12 to 1, 5 and 16, 20, 24, 28 to 2, 6, 3, 7.  Other
+// bits of x0, x1 must be clear.
+__device__ __forceinline__ uint32_t gather_bit7(uint32_t x0, uint32_t x1) {
+  uint32_t d = (x0 >> 7) | (x1 >> 3);
+  d |= d >> 7;
+  d |= d >> 14;
+  return d & 0xFFu;
+}
+
+// pos and neg bytes of 8 int8 values t (two words): bit 7 of
+// (t & 0x7F) + 0x7F is set iff the byte is nonzero; pos = nonzero with the
+// sign clear, neg = sign set (t < 0).
+__device__ __forceinline__ void t2_chunk_bits(uint32_t w0, uint32_t w1, uint32_t& pb,
+                                              uint32_t& nb) {
+  const uint32_t z0 = (w0 & 0x7F7F7F7Fu) + 0x7F7F7F7Fu, z1 = (w1 & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+  pb = gather_bit7(z0 & ~w0 & 0x80808080u, z1 & ~w1 & 0x80808080u);
+  nb = gather_bit7(w0 & 0x80808080u, w1 & 0x80808080u);
+}
+
 __global__ __launch_bounds__(kBlock) void pack_t2_kernel(
     const int8_t* __restrict__ t, const uint16_t* __restrict__ s, int64_t n, int64_t k,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
@@ -118,13 +140,7 @@ __global__ __launch_bounds__(kBlock) void pack_t2_kernel(
     uint32_t pb = 0u, nb = 0u;
     if (row < n) {
       const uint2 v = *reinterpret_cast<const uint2*>(t + row * k + c * kChunk);
-      const uint32_t words[2] = {v.x, v.y};
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        const int32_t b = (int32_t)(int8_t)((words[j >> 2] >> ((j & 3) * 8)) & 0xFFu);
-        pb |= (uint32_t)(b > 0) << j;
-        nb |= (uint32_t)(b < 0) << j;
-      }
+      t2_chunk_bits(v.x, v.y, pb, nb);
     }
     pos[r >> 2] |= pb << ((r & 3) * 8);
     neg[r >> 2] |= nb << ((r & 3) * 8);
