@@ -164,7 +164,9 @@ constexpr int kKBBytes = kKB / 5;        // 256 base-3 bytes per row and block
 // Thread t writes bytes 16 (t % 16) .. + 15 of the block of row t / 16: their
 // 80 weights are chunks 10 (t % 16) .. + 9, whose pos and neg bytes it reads
 // from LDS; a 1024-entry table maps (pos bits, neg bits) of 5 weights to the
-// byte.
+// byte.  VEC (rows a multiple of 16 bytes long, output 16-byte aligned): the
+// 16 bytes go out as one 16-byte store.
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void t2_to_base3_kernel(const uint8_t* __restrict__ codes,
                                                              const uint16_t* __restrict__ scales,
                                                              int64_t n, int64_t k,
@@ -197,6 +199,7 @@ __global__ __launch_bounds__(kBlock) void t2_to_base3_kernel(const uint8_t* __re
     __syncthreads();
     if (row >= n) continue;
     // the 80 pos / neg bits of this thread's weights, in two 40-bit halves
+    uint32_t ob[4] = {0u, 0u, 0u, 0u};  // the thread's 16 bytes
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint64_t P = 0, N = 0;
@@ -208,10 +211,20 @@ __global__ __launch_bounds__(kBlock) void t2_to_base3_kernel(const uint8_t* __re
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int64_t jo = k0 / 5 + bg * 16 + h * 8 + jj;  // byte of the row
-        if (jo < rb)
-          out[row * rb + jo] = byte_of[(((P >> (5 * jj)) & 31) << 5) | ((N >> (5 * jj)) & 31)];
+        const uint32_t v = byte_of[(((P >> (5 * jj)) & 31) << 5) | ((N >> (5 * jj)) & 31)];
+        ob[(h * 8 + jj) >> 2] |= v << (8 * (jj & 3));
       }
+    }
+    const int64_t jo = k0 / 5 + bg * 16;  // first byte of the row
+    if constexpr (VEC) {
+      // rb and jo are multiples of 16: the 16 bytes are all in the row or
+      // all past it
+      if (jo < rb)
+        *reinterpret_cast<uint4*>(out + row * rb + jo) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (jo + i < rb) out[row * rb + jo + i] = (uint8_t)(ob[i >> 2] >> (8 * (i & 3)));
     }
   }
   for (int i = t; i < kTileRows * groups; i += kBlock) {
@@ -223,57 +236,72 @@ __global__ __launch_bounds__(kBlock) void t2_to_base3_kernel(const uint8_t* __re
 
 // base-3 bytes + row-major scales -> two-plane codes + tile-major scales.  The
 // block's 16 row segments are staged in LDS (rows past n as byte 121: every
-// digit 1, t = 0).  An item (chunk, row) takes the two or three bytes that
-// hold its 8 weights, looks up their digits (a table of the five digits of
-// every byte value; a byte of 243..255 decodes with its fifth digit taken
-// mod 3) and writes its pos and neg bytes into the block's cells in LDS,
-// which then go out as whole 16-byte vectors.
+// digit 1, t = 0; VEC as one 16-byte load per thread).  A 256-entry table
+// gives the five pos bits (digit 2) and neg bits (digit 0) of every byte
+// value, pos in bits 0..4 and neg in bits 16..20 (a byte of 243..255 decodes
+// with its fifth digit taken mod 3).  An item (chunk, row) ORs the entries of
+// the three bytes that hold its 8 weights, shifted by 0, 5 and 10, and cuts
+// its pos and neg bytes out of the 15-bit runs at the chunk's first digit;
+// the bytes go into the block's cells in LDS, which then go out as whole
+// 16-byte vectors.
+constexpr int kSegPitch = kKBBytes + 16;  // LDS row: 256 bytes + the item's third byte past the end
+
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void base3_to_t2_kernel(const uint8_t* __restrict__ in,
                                                              const uint16_t* __restrict__ in_scales,
                                                              int64_t n, int64_t k,
                                                              uint8_t* __restrict__ codes,
                                                              uint16_t* __restrict__ scales) {
-  __shared__ uint8_t seg[kTileRows][kKBBytes];
+  __shared__ uint4 segv[kTileRows * kSegPitch / 16];
   __shared__ uint4 cells[kKBChunks * 2];
-  __shared__ uint16_t digits[256];  // digit q (= t + 1) in bits 2q, 2q + 1
+  __shared__ uint32_t pn[256];
   const int64_t tile = blockIdx.x;
   const int64_t chunks = k / kChunk, groups = k / kGroup, rb = (k + 4) / 5;
   const int t = threadIdx.x;
   {
-    int d = t, code = 0;
+    int d = t;
+    uint32_t pos = 0u, neg = 0u;
     for (int q = 0; q < 5; ++q) {
-      code |= (d % 3) << (2 * q);
+      const int dg = d % 3;  // t + 1 of weight q
+      pos |= (uint32_t)(dg == 2) << q;
+      neg |= (uint32_t)(dg == 0) << q;
       d /= 3;
     }
-    digits[t] = (uint16_t)code;
+    pn[t] = pos | (neg << 16);
   }
+  uint8_t* seg = reinterpret_cast<uint8_t*>(segv);
   uint8_t* cb = reinterpret_cast<uint8_t*>(cells);
   for (int64_t k0 = 0; k0 < k; k0 += kKB) {
     const int64_t c0 = k0 / kChunk;
     const int nc = (int)(chunks - c0 < kKBChunks ? chunks - c0 : kKBChunks);
     __syncthreads();  // the previous block's segments and cells have been read
-    for (int i = t; i < kTileRows * kKBBytes; i += kBlock) {
-      const int rr = i / kKBBytes, jb = i % kKBBytes;
-      const int64_t rw = tile * kTileRows + rr, jo = k0 / 5 + jb;
-      seg[rr][jb] = (rw < n && jo < rb) ? in[rw * rb + jo] : (uint8_t)121;
+    if constexpr (VEC) {
+      // thread t: row t / 16, bytes 16 (t % 16) .. + 15 of its segment; rb
+      // and the offsets are multiples of 16, so a vector is all in the row
+      // or all past it
+      const int rr = t >> 4, vj = t & 15;
+      const int64_t rw = tile * kTileRows + rr, jo = k0 / 5 + vj * 16;
+      uint4 v = make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u);
+      if (rw < n && jo < rb) v = *reinterpret_cast<const uint4*>(in + rw * rb + jo);
+      segv[(rr * kSegPitch) / 16 + vj] = v;
+    } else {
+      for (int i = t; i < kTileRows * kKBBytes; i += kBlock) {
+        const int rr = i / kKBBytes, jb = i % kKBBytes;
+        const int64_t rw = tile * kTileRows + rr, jo = k0 / 5 + jb;
+        seg[rr * kSegPitch + jb] = (rw < n && jo < rb) ? in[rw * rb + jo] : (uint8_t)121;
+      }
     }
     __syncthreads();
     for (int it = t; it < nc * kTileRows; it += kBlock) {
       const int c = it >> 4, rr = it & 15;
-      const int j0 = (c * kChunk) / 5, j1 = (c * kChunk + kChunk - 1) / 5;
-      // digits of bytes j0 .. j1 (at most three), 10 bits per byte
-      uint32_t dw = digits[seg[rr][j0]] | ((uint32_t)digits[seg[rr][j0 + 1]] << 10);
-      if (j1 > j0 + 1) dw |= (uint32_t)digits[seg[rr][j0 + 2]] << 20;
+      const int j0 = (c * kChunk) / 5;
       const int off = c * kChunk - 5 * j0;  // digit of weight 0 of the chunk
-      uint32_t pb = 0u, nb = 0u;
-#pragma unroll
-      for (int b = 0; b < kChunk; ++b) {
-        const uint32_t dg = (dw >> (2 * (off + b))) & 3u;  // t + 1
-        pb |= (uint32_t)(dg == 2u) << b;
-        nb |= (uint32_t)(dg == 0u) << b;
-      }
-      cb[c * 32 + rr] = (uint8_t)pb;
-      cb[c * 32 + 16 + rr] = (uint8_t)nb;
+      const uint8_t* sr = seg + rr * kSegPitch + j0;
+      // bytes j0, j0 + 1 and j0 + 2 (the last only when off >= 3; at the
+      // block's end it is padding, whose bits are never cut out)
+      const uint32_t e = pn[sr[0]] | (pn[sr[1]] << 5) | (pn[sr[2]] << 10);
+      cb[c * 32 + rr] = (uint8_t)(e >> off);
+      cb[c * 32 + 16 + rr] = (uint8_t)(e >> (16 + off));
     }
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(codes + (tile * chunks + c0) * 32);
@@ -303,19 +331,33 @@ hipError_t launch_quantize_t2(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
   return hipGetLastError();
 }
 
+// 16-byte row vectors of the base-3 buffer: rows a multiple of 16 bytes
+// long (k a multiple of 80) and the buffer 16-byte aligned
+static bool base3_vec(const void* p, int64_t k) {
+  return ((k + 4) / 5) % 16 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
 hipError_t launch_t2_to_base3(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
                               uint8_t* out, uint16_t* out_scales, hipStream_t st) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL(t2_to_base3_kernel, dim3((unsigned)tiles), dim3(kBlock), 0, st, codes,
-                     scales, n, k, out, out_scales);
+  if (base3_vec(out, k))
+    hipLaunchKernelGGL(t2_to_base3_kernel<true>, dim3((unsigned)tiles), dim3(kBlock), 0, st,
+                       codes, scales, n, k, out, out_scales);
+  else
+    hipLaunchKernelGGL(t2_to_base3_kernel<false>, dim3((unsigned)tiles), dim3(kBlock), 0, st,
+                       codes, scales, n, k, out, out_scales);
   return hipGetLastError();
 }
 
 hipError_t launch_base3_to_t2(const uint8_t* in, const uint16_t* in_scales, int64_t n, int64_t k,
                               uint8_t* codes, uint16_t* scales, hipStream_t st) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL(base3_to_t2_kernel, dim3((unsigned)tiles), dim3(kBlock), 0, st, in,
-                     in_scales, n, k, codes, scales);
+  if (base3_vec(in, k))
+    hipLaunchKernelGGL(base3_to_t2_kernel<true>, dim3((unsigned)tiles), dim3(kBlock), 0, st, in,
+                       in_scales, n, k, codes, scales);
+  else
+    hipLaunchKernelGGL(base3_to_t2_kernel<false>, dim3((unsigned)tiles), dim3(kBlock), 0, st, in,
+                       in_scales, n, k, codes, scales);
   return hipGetLastError();
 }
 
