@@ -125,29 +125,38 @@ __device__ __forceinline__ void t2_chunk_bits(uint32_t w0, uint32_t w1, uint32_t
   nb = gather_bit7(w0 & 0x80808080u, w1 & 0x80808080u);
 }
 
+// One lane per two adjacent chunks (c, c + 1) of a 16-row tile: a 16-byte
+// load of int8 t per row (t is 16-byte aligned and rows are k bytes, a
+// multiple of 128), two cells written.
 __global__ __launch_bounds__(kBlock) void pack_t2_kernel(
     const int8_t* __restrict__ t, const uint16_t* __restrict__ s, int64_t n, int64_t k,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
   const int64_t chunks = k / kChunk;
-  const int64_t cblocks = (k / kChunk + kBlock - 1) / kBlock;
+  const int64_t pairs = chunks / 2;  // chunks % 16 == 0
+  const int64_t cblocks = (pairs + kBlock - 1) / kBlock;
   const int64_t tile = blockIdx.x / cblocks;
-  const int64_t c = (int64_t)(blockIdx.x - tile * cblocks) * kBlock + threadIdx.x;
+  const int64_t c = 2 * ((int64_t)(blockIdx.x - tile * cblocks) * kBlock + threadIdx.x);
   if (c >= chunks) return;
-  uint32_t pos[4] = {0u, 0u, 0u, 0u}, neg[4] = {0u, 0u, 0u, 0u};
+  uint32_t pos[2][4] = {}, neg[2][4] = {};
 #pragma unroll
   for (int r = 0; r < kTileRows; ++r) {
     const int64_t row = tile * kTileRows + r;
-    uint32_t pb = 0u, nb = 0u;
+    uint32_t pb0 = 0u, nb0 = 0u, pb1 = 0u, nb1 = 0u;
     if (row < n) {
-      const uint2 v = *reinterpret_cast<const uint2*>(t + row * k + c * kChunk);
-      t2_chunk_bits(v.x, v.y, pb, nb);
+      const uint4 v = *reinterpret_cast<const uint4*>(t + row * k + c * kChunk);
+      t2_chunk_bits(v.x, v.y, pb0, nb0);
+      t2_chunk_bits(v.z, v.w, pb1, nb1);
     }
-    pos[r >> 2] |= pb << ((r & 3) * 8);
-    neg[r >> 2] |= nb << ((r & 3) * 8);
+    pos[0][r >> 2] |= pb0 << ((r & 3) * 8);
+    neg[0][r >> 2] |= nb0 << ((r & 3) * 8);
+    pos[1][r >> 2] |= pb1 << ((r & 3) * 8);
+    neg[1][r >> 2] |= nb1 << ((r & 3) * 8);
   }
-  uint8_t* cell = codes + (tile * chunks + c) * 32;
-  *reinterpret_cast<uint4*>(cell) = make_uint4(pos[0], pos[1], pos[2], pos[3]);
-  *reinterpret_cast<uint4*>(cell + 16) = make_uint4(neg[0], neg[1], neg[2], neg[3]);
+  uint4* cell = reinterpret_cast<uint4*>(codes + (tile * chunks + c) * 32);
+  cell[0] = make_uint4(pos[0][0], pos[0][1], pos[0][2], pos[0][3]);
+  cell[1] = make_uint4(neg[0][0], neg[0][1], neg[0][2], neg[0][3]);
+  cell[2] = make_uint4(pos[1][0], pos[1][1], pos[1][2], pos[1][3]);
+  cell[3] = make_uint4(neg[1][0], neg[1][1], neg[1][2], neg[1][3]);
 
   // one lane per group copies the 16 rows' scales of that group
   if (c % kChunksPerGroup == 0) {
@@ -238,8 +247,10 @@ hipError_t launch_quantize_q1(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
 
 hipError_t launch_pack_t2(const int8_t* t, const uint16_t* s, int64_t n, int64_t k,
                           uint8_t* codes, uint16_t* scales, hipStream_t st) {
-  hipLaunchKernelGGL(pack_t2_kernel, pack_grid(n, k), dim3(kBlock), 0, st, t, s, n, k, codes,
-                     scales);
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t pairs = k / kChunk / 2;
+  hipLaunchKernelGGL(pack_t2_kernel, dim3((unsigned)(tiles * ((pairs + kBlock - 1) / kBlock))),
+                     dim3(kBlock), 0, st, t, s, n, k, codes, scales);
   return hipGetLastError();
 }
 
