@@ -6,13 +6,15 @@
 // [P2] 7minutos.es, "PrismML lanza Bonsai 27B ...", section "Como funciona la
 //      compresion": w = s_g * t_i with t in {-1, 0, +1}.
 //
-// Thread mapping (all three kernels): one lane per 8-weight chunk c of one
-// 16-row tile.  For a fixed row, the 256 lanes of a block touch 256 adjacent
-// chunks, i.e. 4 KB (FP16 in), 2 KB (int8 in) or 4 KB (FP16 out) of one row:
-// every global access is a contiguous, 16-byte-per-lane sweep.  Each lane
-// then writes its whole 16- or 32-byte code cell with one or two 16-byte
-// stores, which are again contiguous across lanes.  The work is bound by HBM;
-// the bit logic costs a few ALU operations per weight.
+// Thread mapping: one lane per 8-weight chunk c of one 16-row tile (the
+// quantiser and the unpacker; the ternary packer takes two adjacent chunks
+// per lane, so that its int8 input also comes in 16 bytes per lane).  For a
+// fixed row, the 128 lanes of a work-group touch adjacent chunks, i.e. 2 KB
+// (FP16 in), 2 KB (int8 in, two chunks per lane) or 2 KB (FP16 out) of one
+// row: every global access is a contiguous, 16-byte-per-lane sweep.  Each
+// lane then writes its whole 16- or 32-byte code cell(s) with 16-byte stores,
+// which are again contiguous across lanes.  The work is bound by HBM; the bit
+// logic runs two FP16 or four int8 values per instruction.
 #include "common.h"
 
 namespace lowbit {
