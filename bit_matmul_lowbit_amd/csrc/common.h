@@ -147,6 +147,14 @@ hipError_t launch_gemv_mfma_prepare(int64_t n, int64_t k, const uint16_t* x, int
 hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
                             int64_t k, int64_t b, float* y, const void* ws, int cus,
                             hipStream_t st);
+// b >= kMfmaMinBatch, the decode FFN's gate+up GEMV: W x with x FP16
+// [b][k] read in place (no prepare), stored as one FP32 [b][n] plane per
+// K-piece (plain stores: nothing to zero) at hp; *planes receives the
+// number of planes, at most gemv_mfma_max_planes(k)
+int64_t gemv_mfma_max_planes(int64_t k);
+hipError_t launch_gemv_mfma_planes(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                   int64_t n, int64_t k, int64_t b, const uint16_t* x, float* hp,
+                                   int cus, int64_t* planes, hipStream_t st);
 // ceiling probe: the matrix-core GEMV's per-row expansion and MFMA on
 // register data (mode 0: expansion + MFMA, 1: the MFMA alone), `blocks` work-groups
 // of 256 threads
@@ -154,14 +162,21 @@ hipError_t launch_probe_expand_mfma(int mode, int iters, int blocks, float* sink
 size_t gemv_workspace_bytes(int64_t k, int64_t b);
 hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
                                void* ws, hipStream_t st);
-// b < kMfmaMinBatch: the same, and a second range y2[0 .. n2) zeroed too
-hipError_t launch_gemv_prepare_zero2(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
-                                     void* ws, float* y2, int64_t n2, hipStream_t st);
-// b < kMfmaMinBatch: y += W z with z = RNE_fp16(SiLU(gate) * up) formed from
-// h (FP32 [b][2k], gate columns then up columns) inside the GEMV
+// b < kMfmaMinBatch, the decode FFN's table GEMVs.  gemv_partial_planes:
+// the K-slices of the table GEMV for (k, b).  launch_gemv_partials: W x
+// (x FP16 [b][k] read in place) as one FP32 [b][n] plane of partial sums
+// per K-slice, hp = [gemv_partial_planes(k, b)][b][n], written with plain
+// stores; the kernel also zeroes yz[0 .. yzn).  launch_gemv_accumulate_silu:
+// y += W z with z = RNE_fp16(SiLU(gate) * up) formed inside the GEMV from
+// h = the sum of the np planes at hp (FP32 [np][b][2k], gate columns then
+// up columns).
+int64_t gemv_partial_planes(int64_t k, int64_t b);
+hipError_t launch_gemv_partials(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                                int64_t k, int64_t b, const uint16_t* x, float* hp, float* yz,
+                                int64_t yzn, hipStream_t st);
 hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
-                                       int64_t n, int64_t k, int64_t b, float* y, const float* h,
-                                       hipStream_t st);
+                                       int64_t n, int64_t k, int64_t b, float* y, const float* hp,
+                                       int64_t np, hipStream_t st);
 hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t* scales,
                                   int64_t n, int64_t k, int64_t b, float* y, const void* ws,
                                   hipStream_t st);

@@ -30,10 +30,13 @@
 //      rows' scales, reduced over the groups, and added to y with one FP32
 //      atomic per row and K-slice.
 //
-// A second entry (launch_gemv_accumulate_silu, b <= 2) serves the decode
-// FFN's down projection: its activations z = RNE_fp16(SiLU(gate) * up) are
-// formed from the FP32 gate+up result h while the tables are built, so z is
-// never written out.
+// Two more entries serve the decode FFN (b <= 2) as two launches with
+// nothing to zero beforehand: launch_gemv_partials (gate+up) reads x in
+// place and stores each K-slice's row sums into a plane of its own (plain
+// stores, no atomics), zeroing the FFN output as it goes;
+// launch_gemv_accumulate_silu (down) adds those planes up and forms its
+// activations z = RNE_fp16(SiLU(gate) * up) while the tables are built, so
+// neither the sum h nor z is ever written out.
 //
 // With batch b > 1 the 64 lanes are split into BP = 2, 4, 8 column groups of
 // CH = 64 / BP lanes (BP = b rounded up to a power of two); the code cells
@@ -81,16 +84,13 @@ __device__ __forceinline__ int64_t lane_chunk(int64_t s, int lanec, int ch, int 
 }
 
 // prepare: x [b][k] -> workspace (read by the main kernel's table build), y = 0
-// (and y2 = 0 when given: the decode FFN zeroes its output here too)
 __global__ __launch_bounds__(kWG) void gemv_prepare_kernel(const uint4* __restrict__ x,
                                                            int64_t nvec, uint4* __restrict__ xs,
                                                            float* __restrict__ y,
-                                                           int64_t ycount, float* __restrict__ y2,
-                                                           int64_t ycount2) {
+                                                           int64_t ycount) {
   const int64_t gid = (int64_t)blockIdx.x * kWG + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kWG;
   zero_f32(y, ycount, gid, stride);
-  if (ycount2 > 0) zero_f32(y2, ycount2, gid, stride);
   for (int64_t i = gid; i < nvec; i += stride) xs[i] = x[i];
 }
 
@@ -277,11 +277,13 @@ __device__ __forceinline__ void tile_lookups(const TileRegs<FMT>& tr, const char
 
 // Reduction of a tile's 16 row partials: within the group, scale the two
 // rows each lane is left with (scale word `sw`, zero for inactive lanes),
-// across the groups, then one atomic add per row.  T2 halves its sums here.
-template <int FMT, int CH>
+// across the groups, then one atomic add per row -- or, with PART, a plain
+// store of the slice's partial sum into y + ybase (a [b][n] plane of its
+// own per K-slice).  T2 halves its sums here.
+template <int FMT, int CH, bool PART = false>
 __device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, int lane,
                                            int col, int b, int64_t t, int64_t n,
-                                           float* __restrict__ y) {
+                                           float* __restrict__ y, int64_t ybase = 0) {
   int row_off;
   bool writer;
   reduce_in_group(acc, lane, row_off);
@@ -292,7 +294,12 @@ __device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, int la
 #pragma unroll
   for (int j = 0; j < nv; ++j) {
     const int64_t row = t * kTileRows + row_off + j;
-    if (writer && col < b && row < n) atomicAdd(y + (int64_t)col * n + row, acc[j]);
+    if (writer && col < b && row < n) {
+      if constexpr (PART)
+        y[ybase + (int64_t)col * n + row] = acc[j];
+      else
+        atomicAdd(y + (int64_t)col * n + row, acc[j]);
+    }
   }
 }
 
@@ -304,14 +311,22 @@ __device__ __forceinline__ void tile_store(float (&acc)[16], uint32_t sw, int la
 // block index, so the chip sweeps the code plane front to back in one
 // contiguous front: HBM serves such a sweep measurably faster (about
 // 6.3 TB/s on MI355X) than hundreds of independent streams (about 4.8 TB/s).
-// ZH: the activations are z = RNE_fp16(SiLU(gate) * up) of the decode FFN,
-// formed from h (FP32 [b][2k]: k gate columns, then k up columns) by the
-// table build itself (the same arithmetic as silu_mul_kernel).
-template <int FMT, int CH, bool ZH = false>
+// The decode FFN's two table GEMVs (b <= 2) use two variants:
+// PART (gate+up): slice s stores its partial sums into plane s of y
+//   (FP32 [nslices][b][n]) with plain stores, so that nothing has to be
+//   zeroed first, and the work-groups zero yz[0 .. yzn) (the FFN output, to
+//   which the down GEMV adds) on the way;
+// ZH (down): the activations are z = RNE_fp16(SiLU(gate) * up), formed in
+//   the table build (the same arithmetic as silu_mul_kernel) from h = the
+//   sum of the np planes of partial sums at `h` (FP32 [np][b][2k]: k gate
+//   columns, then k up columns), added in a fixed order (plane order for
+//   np <= 8).
+template <int FMT, int CH, bool ZH = false, bool PART = false>
 __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ xs, float* __restrict__ y, int64_t n, int64_t k, int b,
-    int64_t ntiles, int64_t nslices, const float* __restrict__ h) {
+    int64_t ntiles, int64_t nslices, const float* __restrict__ h, int np,
+    float* __restrict__ yz, int64_t yzn) {
   __shared__ float4 table[kImages * kSliceFloats / 4];
   const int64_t s = blockIdx.x % nslices;
   const int64_t m = blockIdx.x / nslices;
@@ -364,6 +379,9 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
   const int bl = threadIdx.x & 63;        // lane whose table column is built
   const int bq = (threadIdx.x >> 9) & 1;  // image
   const int bp = (threadIdx.x >> 6) & 7;  // hi nibbles 2 bp, 2 bp + 1
+  if constexpr (PART)
+    zero_f32(yz, yzn, (int64_t)blockIdx.x * kMainThreads + threadIdx.x,
+             (int64_t)gridDim.x * kMainThreads);
   uint4 xv4;
   {
     const int bcol = bl / CH;
@@ -376,22 +394,60 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
       const uint32_t xoff = bvalid ? (uint32_t)((bcol * k + bchunk * kChunk) * 2) : 0xFFFFFFF0u;
       xv4 = bload<0>(xr, xoff);
     } else {
-      const __amdgpu_buffer_rsrc_t hr =
-          buffer_rsrc(reinterpret_cast<const uint8_t*>(h), (int64_t)b * 2 * k * 4);
+      // The 8 waves of an image share its 64 chunks: wave bp adds planes
+      // bp, bp + 8, ... of its lane's chunk (gate and up, 16 floats) and
+      // stages the sums in LDS (image 0 of the table, not yet built:
+      // float4 i of wave (bp, bq), lane L at (i * 16 + 2 bp + bq) * 64 + L,
+      // conflict-free); wave 0 of each image adds the staged sums in wave
+      // order, forms z and leaves it in zsh for the whole work-group.  The
+      // build needs z: every wave waits for it here, before any weight load
+      // goes out (as for x above).
+      __shared__ uint4 zsh[kImages * kLanes];
+      const int bw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+      const int wp = bw & 7;  // = bp, known to be wave-uniform
+      const int npw = np < 8 ? np : 8;
       const uint32_t go = bvalid ? (uint32_t)((bcol * 2 * k + bchunk * kChunk) * 4) : 0xFFFFFFE0u;
       const uint32_t uo = bvalid ? go + (uint32_t)(k * 4) : 0xFFFFFFE0u;
-      const uint4 g0 = bload<0>(hr, go), g1 = bload<16>(hr, go);
-      const uint4 u0 = bload<0>(hr, uo), u1 = bload<16>(hr, uo);
-      // the build needs the product: wait for h here, before any weight
-      // load goes out (as for x above)
-      __asm__ volatile("" ::"v"(g0.x), "v"(g0.y), "v"(g0.z), "v"(g0.w), "v"(g1.x), "v"(g1.y),
-                       "v"(g1.z), "v"(g1.w), "v"(u0.x), "v"(u0.y), "v"(u0.z), "v"(u0.w), "v"(u1.x),
-                       "v"(u1.y), "v"(u1.z), "v"(u1.w));
-      const float gv[8] = {u2f(g0.x), u2f(g0.y), u2f(g0.z), u2f(g0.w),
-                           u2f(g1.x), u2f(g1.y), u2f(g1.z), u2f(g1.w)};
-      const float uv[8] = {u2f(u0.x), u2f(u0.y), u2f(u0.z), u2f(u0.w),
-                           u2f(u1.x), u2f(u1.y), u2f(u1.z), u2f(u1.w)};
-      xv4 = silu_mul8(gv, uv);
+      const int64_t plane = (int64_t)b * 2 * k;  // floats per plane
+      if (wp < npw) {
+        float4 a[4] = {};
+        for (int p = wp; p < np; p += 8) {
+          const __amdgpu_buffer_rsrc_t hr =
+              buffer_rsrc(reinterpret_cast<const uint8_t*>(h + p * plane), plane * 4);
+          const uint4 v[4] = {bload<0>(hr, go), bload<16>(hr, go), bload<0>(hr, uo),
+                              bload<16>(hr, uo)};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i].x += u2f(v[i].x);
+            a[i].y += u2f(v[i].y);
+            a[i].z += u2f(v[i].z);
+            a[i].w += u2f(v[i].w);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) table[(i * 16 + 2 * wp + bq) * 64 + bl] = a[i];
+      }
+      __syncthreads();
+      if (wp == 0) {
+        float4 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = table[(i * 16 + bq) * 64 + bl];
+        for (int w = 1; w < npw; ++w) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 v = table[(i * 16 + 2 * w + bq) * 64 + bl];
+            a[i].x += v.x;
+            a[i].y += v.y;
+            a[i].z += v.z;
+            a[i].w += v.w;
+          }
+        }
+        const float gv[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
+        const float uv[8] = {a[2].x, a[2].y, a[2].z, a[2].w, a[3].x, a[3].y, a[3].z, a[3].w};
+        zsh[bq * kLanes + bl] = silu_mul8(gv, uv);
+      }
+      __syncthreads();
+      xv4 = zsh[bq * kLanes + bl];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -451,7 +507,7 @@ __global__ __launch_bounds__(kMainThreads, kMainWaves / 4) void gemv_main_kernel
     load_next(buf[(i + D - 1) % D]);
     tile_lookups<FMT>(buf[(i + 1) % D], tbase, lane_base, nxt);
     const uint32_t sw_nxt = active ? buf[(i + 1) % D].sc : 0u;
-    tile_store<FMT, CH>(cur, sw_cur, lane, col, b, t, n, y);
+    tile_store<FMT, CH, PART>(cur, sw_cur, lane, col, b, t, n, y, PART ? s * b * n : 0);
     sw_cur = sw_nxt;
     t += stride;
   };
@@ -477,13 +533,23 @@ int64_t nslices_for(int64_t k, int ch) {
   return (chunks + 2 * ch - 1) / (2 * ch);
 }
 
+// grid of the main kernel: G work-groups per slice, about one per CU in
+// all, and no more than there are 16-tile blocks
+dim3 main_grid(int64_t ntiles, int64_t nslices) {
+  int64_t G = (int64_t)device_cu_count() / nslices;
+  if (G < 1) G = 1;
+  const int64_t blocks = (ntiles + kMainWaves - 1) / kMainWaves;
+  if (G > blocks) G = blocks;
+  return dim3((unsigned)(G * nslices));
+}
+
 template <int FMT>
 hipError_t launch_main(int ch, dim3 grid, hipStream_t st, const uint8_t* codes,
                        const uint16_t* scales, const uint16_t* xs, float* y, int64_t n, int64_t k,
                        int b, int64_t ntiles, int64_t nslices) {
 #define LOWBIT_LAUNCH(CHV)                                                                      \
   hipLaunchKernelGGL((gemv_main_kernel<FMT, CHV>), grid, dim3(kMainThreads), 0, st, codes,     \
-                     scales, xs, y, n, k, b, ntiles, nslices, nullptr)
+                     scales, xs, y, n, k, b, ntiles, nslices, nullptr, 0, nullptr, (int64_t)0)
   switch (ch) {
     case 64: LOWBIT_LAUNCH(64); break;
     case 32: LOWBIT_LAUNCH(32); break;
@@ -510,21 +576,7 @@ hipError_t launch_gemv_prepare(int64_t n, int64_t k, const uint16_t* x, int64_t 
   int64_t blocks = (work + kWG - 1) / kWG;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(gemv_prepare_kernel, dim3((unsigned)blocks), dim3(kWG), 0, st,
-                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b,
-                     nullptr, (int64_t)0);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_prepare_zero2(int64_t n, int64_t k, const uint16_t* x, int64_t b, float* y,
-                                     void* ws, float* y2, int64_t n2, hipStream_t st) {
-  const int64_t nvec = b * k / 8;
-  const int64_t yvec = (n * b + n2 + 3) / 4;
-  const int64_t work = nvec > yvec ? nvec : yvec;
-  int64_t blocks = (work + kWG - 1) / kWG;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(gemv_prepare_kernel, dim3((unsigned)blocks), dim3(kWG), 0, st,
-                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b,
-                     y2, n2);
+                     reinterpret_cast<const uint4*>(x), nvec, static_cast<uint4*>(ws), y, n * b);
   return hipGetLastError();
 }
 
@@ -537,33 +589,46 @@ hipError_t launch_gemv_accumulate(int fmt, const uint8_t* codes, const uint16_t*
   const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
   const uint16_t* xs = static_cast<const uint16_t*>(ws);
-  // G work-groups per slice: about one per CU in all, and no more than there
-  // are 16-tile blocks
-  int64_t G = (int64_t)device_cu_count() / nslices;
-  if (G < 1) G = 1;
-  const int64_t blocks = (ntiles + kMainWaves - 1) / kMainWaves;
-  if (G > blocks) G = blocks;
-  const int64_t nwg = G * nslices;
-  dim3 grid((unsigned)nwg);
+  const dim3 grid = main_grid(ntiles, nslices);
   if (fmt == 1)
     return launch_main<1>(ch, grid, st, codes, scales, xs, y, n, k, (int)b, ntiles, nslices);
   return launch_main<2>(ch, grid, st, codes, scales, xs, y, n, k, (int)b, ntiles, nslices);
 }
 
-hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
-                                       int64_t n, int64_t k, int64_t b, float* y, const float* h,
-                                       hipStream_t st) {
+int64_t gemv_partial_planes(int64_t k, int64_t b) { return nslices_for(k, kLanes / bp_for(b)); }
+
+hipError_t launch_gemv_partials(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                                int64_t k, int64_t b, const uint16_t* x, float* hp, float* yz,
+                                int64_t yzn, hipStream_t st) {
   const int ch = kLanes / bp_for(b);  // 64 or 32: b <= 2
   const int64_t nslices = nslices_for(k, ch);
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
-  int64_t G = (int64_t)device_cu_count() / nslices;
-  if (G < 1) G = 1;
-  const int64_t blocks = (ntiles + kMainWaves - 1) / kMainWaves;
-  if (G > blocks) G = blocks;
-  const dim3 grid((unsigned)(G * nslices));
+  const dim3 grid = main_grid(ntiles, nslices);
+#define LOWBIT_LAUNCH(F, CHV)                                                                   \
+  hipLaunchKernelGGL((gemv_main_kernel<F, CHV, false, true>), grid, dim3(kMainThreads), 0, st,  \
+                     codes, scales, x, hp, n, k, (int)b, ntiles, nslices, nullptr, 0, yz, yzn)
+  if (fmt == 1) {
+    if (ch == 64) LOWBIT_LAUNCH(1, 64);
+    else LOWBIT_LAUNCH(1, 32);
+  } else {
+    if (ch == 64) LOWBIT_LAUNCH(2, 64);
+    else LOWBIT_LAUNCH(2, 32);
+  }
+#undef LOWBIT_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_accumulate_silu(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                       int64_t n, int64_t k, int64_t b, float* y, const float* hp,
+                                       int64_t np, hipStream_t st) {
+  const int ch = kLanes / bp_for(b);  // 64 or 32: b <= 2
+  const int64_t nslices = nslices_for(k, ch);
+  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
+  const dim3 grid = main_grid(ntiles, nslices);
 #define LOWBIT_LAUNCH(F, CHV)                                                                   \
   hipLaunchKernelGGL((gemv_main_kernel<F, CHV, true>), grid, dim3(kMainThreads), 0, st, codes,  \
-                     scales, nullptr, y, n, k, (int)b, ntiles, nslices, h)
+                     scales, nullptr, y, n, k, (int)b, ntiles, nslices, hp, (int)np, nullptr,   \
+                     (int64_t)0)
   if (fmt == 1) {
     if (ch == 64) LOWBIT_LAUNCH(1, 64);
     else LOWBIT_LAUNCH(1, 32);

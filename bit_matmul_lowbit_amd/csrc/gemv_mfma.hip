@@ -130,7 +130,11 @@ struct GroupRegs {
   uint4 x[kSteps];  // A operands of the group's four steps
 };
 
-template <int FMT>
+// x operands: from the prepared workspace (vector (g, j, lane) at
+// ((g * kSteps + j) * 64 + lane) * 16 bytes), or with XD from x itself
+// (FP16 [b][k]: the lane's batch row and chunk 16 g + 4 j + q, i.e. the
+// lane offset row * 2k + 16 q plus 256 g + 64 j)
+template <int FMT, bool XD = false>
 __device__ __forceinline__ void load_group(GroupRegs<FMT>& r, __amdgpu_buffer_rsrc_t rc,
                                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rx,
                                            uint32_t voff_c, uint32_t voff_s, uint32_t voff_x,
@@ -143,7 +147,8 @@ __device__ __forceinline__ void load_group(GroupRegs<FMT>& r, __amdgpu_buffer_rs
   r.s[0] = bload<0>(rs, voff_s, g * 32);
   r.s[1] = bload<16>(rs, voff_s, g * 32);
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j) r.x[j] = bload(rx, voff_x, (g * kSteps + j) * kXStep);
+  for (int j = 0; j < kSteps; ++j)
+    r.x[j] = bload(rx, voff_x, XD ? g * 256 + j * 64 : (g * kSteps + j) * kXStep);
 }
 
 // the scale of row rho in both halves
@@ -214,7 +219,11 @@ __global__ __launch_bounds__(256) void gemv_mfma_prepare_kernel(const uint16_t* 
   }
 }
 
-template <int FMT>
+// XD (the decode FFN's gate+up GEMV): x is read as given (FP16 [b][k], no
+// prepare launch) and each item stores its K-piece's sums into plane
+// `piece` of y (FP32 [kpieces][b][n]) instead of adding them up, so y
+// needs no zeroing.
+template <int FMT, bool XD = false>
 __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint4* __restrict__ xw, float* __restrict__ y, int64_t n, int64_t k, int b,
@@ -233,8 +242,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   const int64_t spitch = (int64_t)G * kTileRows * 2;
   const uint32_t voff_c = (uint32_t)(tl * cpitch + q * Fmt<FMT>::cell_bytes);
   const uint32_t voff_s = (uint32_t)(tl * spitch);
-  const uint32_t voff_x = tl < b ? (uint32_t)(lane * 16) : kNoLoad;
-  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xw, (int64_t)G * kSteps * kXStep);
+  const uint32_t voff_x =
+      tl < b ? (XD ? (uint32_t)(tl * k * 2 + q * 16) : (uint32_t)(lane * 16)) : kNoLoad;
+  const __amdgpu_buffer_rsrc_t rx =
+      buffer_rsrc(xw, XD ? (int64_t)b * k * 2 : (int64_t)G * kSteps * kXStep);
   const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(xw, 0);  // all loads return zero
 
   // This work-group's items: blockIdx.x + i * gridDim.x.  Every wave runs
@@ -260,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + T0 * cpitch, here * cpitch);
     const __amdgpu_buffer_rsrc_t rs =
         buffer_rsrc(reinterpret_cast<const uint8_t*>(scales) + T0 * spitch, here * spitch);
-    load_group<FMT>(r, live ? rc : rz, live ? rs : rz, live ? rx : rz, voff_c, voff_s, voff_x,
-                    live ? g : 0);
+    load_group<FMT, XD>(r, live ? rc : rz, live ? rs : rz, live ? rx : rz, voff_c, voff_s,
+                        voff_x, live ? g : 0);
   };
 
   f32x4 acc[16];
@@ -308,9 +319,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
         }
         if (row < n) {
           const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          const int64_t pb = XD ? (item % kpieces) * b : 0;  // plane of this K-piece
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (i < b) atomicAdd(y + i * n + row, sv[i]);
+          for (int i = 0; i < 8; ++i) {
+            if (i < b) {
+              if constexpr (XD)
+                y[(pb + i) * n + row] = sv[i];
+              else
+                atomicAdd(y + i * n + row, sv[i]);
+            }
+          }
         }
         rb ^= 1;
       }
@@ -336,7 +354,8 @@ struct CodeRegs {
   uint4 s[2];
 };
 
-template <int FMT>
+// XD as for gemv_mfma_kernel: x as given, K-piece sums stored into planes
+template <int FMT, bool XD = false>
 __global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint4* __restrict__ xw, float* __restrict__ y, int64_t n, int64_t k, int b,
@@ -380,8 +399,17 @@ __global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_ker
   }
   // the item's x operands into LDS: vector (group gl, step j, lane l) at
   // (gl * kSteps + j) * 64 + l
-  for (int i = threadIdx.x; i < ng * kSteps * 64; i += kThreads)
-    lds[i] = (i & 15) < b ? xw[(int64_t)g0 * kSteps * 64 + i] : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < ng * kSteps * 64; i += kThreads) {
+    if constexpr (XD) {
+      // batch row l % 16, chunk 16 (g0 + gl) + 4 j + l / 16 of x [b][k]
+      const int l = i & 63, gl = i / (kSteps * 64), j = (i >> 6) % kSteps;
+      const int64_t chunk = (int64_t)(g0 + gl) * 16 + 4 * j + (l >> 4);
+      lds[i] = (l & 15) < b ? xw[((int64_t)(l & 15) * k + chunk * kChunk) / 8]
+                            : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      lds[i] = (i & 15) < b ? xw[(int64_t)g0 * kSteps * 64 + i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   __syncthreads();
 
   f32x4 acc[16];
@@ -420,11 +448,15 @@ __global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_ker
   const int64_t row = T0 * 16 + t;
   const int rr = (t & 15) * 16 + (t >> 4);
   if (row < n) {
+    const int64_t pb = XD ? (item % kpieces) * b : 0;  // plane of this K-piece
     for (int i = 0; i < b; ++i) {
       float sum = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) sum += red[(w * 8 + i) * kRedPitch + rr];
-      atomicAdd(y + i * n + row, sum);
+      if constexpr (XD)
+        y[(pb + i) * n + row] = sum;
+      else
+        atomicAdd(y + i * n + row, sum);
     }
   }
 }
@@ -490,57 +522,91 @@ hipError_t launch_gemv_mfma_prepare(int64_t n, int64_t k, const uint16_t* x, int
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
-                            int64_t k, int64_t b, float* y, const void* ws, int cus,
-                            hipStream_t st) {
-  const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t nblocks = (ntiles + 15) / 16;
+namespace {
+
+// Work split of the matrix-core GEMV.  Persistent grid of up to two
+// work-groups per CU.  An item's K-piece is 4 * per groups (per groups for
+// each wave): per is chosen for about four items per work-group, but at
+// least two groups per wave (each item ends with an LDS reduction and
+// atomics) and no more than K holds.  The grid is two work-groups per CU
+// (fewer only if there are fewer items), all resident at once, so a
+// work-group with a second item has its loads in flight while it finishes
+// the first; one work-group per item, with the items past the resident ones
+// launched as a second round, ran the 27B gate+up (680 items) at b = 5 / 8
+// in 15.0-15.5 / 15.5-16.0 us instead of 14.3 / 14.7 us.  A matrix whose
+// two-group items would not even give every CU one takes a single group per
+// wave (twice the items): 6144x2048 ternary at b = 3..8 runs 12.2 -> 11.1
+// us, while larger matrices lose with it (27B gate+up at b = 5: 19 us).
+struct MfmaPlan {
+  int64_t ntiles, kp, nitems, nwg;
+  int gpp;
+  bool item;  // one item per work-group (gemv_mfma_item_kernel)
+};
+
+MfmaPlan mfma_plan(int64_t n, int64_t k, int cus) {
+  MfmaPlan p;
+  p.ntiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t nblocks = (p.ntiles + 15) / 16;
   const int G = (int)(k / kGroup);
-  // Persistent grid of up to two work-groups per CU.  An item's K-piece is
-  // 4 * per groups (per groups for each wave): per is chosen for about four
-  // items per work-group, but at least two groups per wave (each item ends
-  // with an LDS reduction and atomics) and no more than K holds.  The grid
-  // is two work-groups per CU (fewer only if there are fewer items), all
-  // resident at once, so a work-group with a second item has its loads in
-  // flight while it finishes the first; one work-group per item, with the
-  // items past the resident ones launched as a second round, ran the 27B
-  // gate+up (680 items) at b = 5 / 8 in 15.0-15.5 / 15.5-16.0 us instead
-  // of 14.3 / 14.7 us.  A matrix whose two-group items would not even give
-  // every CU one takes a single group per wave (twice the items):
-  // 6144x2048 ternary at b = 3..8 runs 12.2 -> 11.1 us, while larger
-  // matrices lose with it (27B gate+up at b = 5: 19 us).
   const int64_t nwg_max = 2 * (int64_t)cus;
   int64_t per = (int64_t)G * nblocks / (4 * kWaves * nwg_max);
   const int64_t per_max = (G + kWaves - 1) / kWaves;
   if (per < 2) per = nblocks * ((G + 2 * kWaves - 1) / (2 * kWaves)) < cus ? 1 : 2;
   if (per > per_max) per = per_max;
-  const int gpp = (int)(kWaves * per);
-  const int64_t kp = (G + gpp - 1) / gpp;
-  const int64_t nitems = nblocks * kp;
-  const int64_t nwg = nitems < nwg_max ? nitems : nwg_max;
-  const uint4* xw = static_cast<const uint4*>(ws);
+  p.gpp = (int)(kWaves * per);
+  p.kp = (G + p.gpp - 1) / p.gpp;
+  p.nitems = nblocks * p.kp;
+  p.nwg = p.nitems < nwg_max ? p.nitems : nwg_max;
   // no more items than CUs: one item per work-group, x from LDS (ternary
   // 6144x2048 and 2048x6144 at b = 5: 11.1 -> 9.0 us; the 27B-class
   // matrices, 340 and 680 items, ran 12-15 % slower this way than with the
-  // persistent kernel below and stay on it)
-  if (gpp <= kItemMaxGroups && nitems <= (int64_t)cus) {
-    const dim3 igrid((unsigned)nitems);
+  // persistent kernel and stay on it)
+  p.item = p.gpp <= kItemMaxGroups && p.nitems <= (int64_t)cus;
+  return p;
+}
+
+template <bool XD>
+hipError_t launch_plan(const MfmaPlan& p, int fmt, const uint8_t* codes, const uint16_t* scales,
+                       int64_t n, int64_t k, int64_t b, float* y, const uint4* xin,
+                       hipStream_t st) {
+  if (p.item) {
+    const dim3 igrid((unsigned)p.nitems);
     if (fmt == 1)
-      hipLaunchKernelGGL(gemv_mfma_item_kernel<1>, igrid, dim3(kThreads), 0, st, codes, scales, xw,
-                         y, n, k, (int)b, ntiles, (int)kp, gpp);
+      hipLaunchKernelGGL((gemv_mfma_item_kernel<1, XD>), igrid, dim3(kThreads), 0, st, codes,
+                         scales, xin, y, n, k, (int)b, p.ntiles, (int)p.kp, p.gpp);
     else
-      hipLaunchKernelGGL(gemv_mfma_item_kernel<2>, igrid, dim3(kThreads), 0, st, codes, scales, xw,
-                         y, n, k, (int)b, ntiles, (int)kp, gpp);
+      hipLaunchKernelGGL((gemv_mfma_item_kernel<2, XD>), igrid, dim3(kThreads), 0, st, codes,
+                         scales, xin, y, n, k, (int)b, p.ntiles, (int)p.kp, p.gpp);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)nwg);
+  const dim3 grid((unsigned)p.nwg);
   if (fmt == 1)
-    hipLaunchKernelGGL(gemv_mfma_kernel<1>, grid, dim3(kThreads), 0, st, codes, scales, xw, y, n,
-                       k, (int)b, ntiles, (int)kp, gpp, nitems);
+    hipLaunchKernelGGL((gemv_mfma_kernel<1, XD>), grid, dim3(kThreads), 0, st, codes, scales, xin,
+                       y, n, k, (int)b, p.ntiles, (int)p.kp, p.gpp, p.nitems);
   else
-    hipLaunchKernelGGL(gemv_mfma_kernel<2>, grid, dim3(kThreads), 0, st, codes, scales, xw, y, n,
-                       k, (int)b, ntiles, (int)kp, gpp, nitems);
+    hipLaunchKernelGGL((gemv_mfma_kernel<2, XD>), grid, dim3(kThreads), 0, st, codes, scales, xin,
+                       y, n, k, (int)b, p.ntiles, (int)p.kp, p.gpp, p.nitems);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t n,
+                            int64_t k, int64_t b, float* y, const void* ws, int cus,
+                            hipStream_t st) {
+  return launch_plan<false>(mfma_plan(n, k, cus), fmt, codes, scales, n, k, b, y,
+                            static_cast<const uint4*>(ws), st);
+}
+
+int64_t gemv_mfma_max_planes(int64_t k) { return (k / kGroup + kWaves - 1) / kWaves; }
+
+hipError_t launch_gemv_mfma_planes(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                   int64_t n, int64_t k, int64_t b, const uint16_t* x, float* hp,
+                                   int cus, int64_t* planes, hipStream_t st) {
+  const MfmaPlan p = mfma_plan(n, k, cus);
+  *planes = p.kp;
+  return launch_plan<true>(p, fmt, codes, scales, n, k, b, hp, reinterpret_cast<const uint4*>(x),
+                           st);
 }
 
 }  // namespace lowbit

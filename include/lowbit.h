@@ -306,13 +306,17 @@ size_t lowbit_ffn_workspace_bytes(int fmt, int64_t k, int64_t f, int64_t b);
  *   workspace : at least lowbit_ffn_workspace_bytes(fmt, k, f, b) bytes of
  *               device scratch, contents ignored on entry and clobbered.
  * When both matrices are within lowbit_gemv's single-kernel limits the
- * chain is two kernels, the second forming z itself; otherwise, for b <= 2,
- * z is formed inside the down GEMV, and for b >= 3 by its own launch.  z
- * is never written out except by that launch, and always with the
- * arithmetic of lowbit_silu_mul.
+ * chain is two kernels, the second forming z itself.  Otherwise, for
+ * b <= 2, it is two kernels too: the gate+up GEMV stores the partial sums
+ * of each of its K-slices (no atomics; it also zeroes y) and the down GEMV
+ * adds them up in a fixed order and forms z inside its own table build;
+ * for b >= 3, z is formed by a launch of its own.  z is never written out
+ * except by that launch, and always with the arithmetic of
+ * lowbit_silu_mul.
  * Both matrices use format fmt; k and f must be multiples of 128.  As in
- * lowbit_gemv, K-slices are combined with atomic adds on the larger
- * shapes, so the last bits of h and y may differ from run to run, and so
+ * lowbit_gemv, the down GEMV's K-slices are combined with atomic adds on
+ * the larger shapes (and, for b >= 3, the gate+up GEMV's too), so the last
+ * bits of y may differ from run to run, and for b >= 3 those of h, and so
  * may a z value that lies on an FP16 rounding boundary. */
 int lowbit_ffn(int fmt, const void* gu_codes, const uint16_t* gu_scales,
                const void* dn_codes, const uint16_t* dn_scales, int64_t k, int64_t f,

@@ -85,10 +85,20 @@ def test_silu_mul_matches_oracle():
 # shapes whose matrices are both small run the two single-launch GEMVs;
 # f = 8320 (> 8192) or, for b >= 2, f = 4224 (> 4096) puts the down matrix
 # past that kernel's limit, so those shapes run the table (b <= 2) or
-# matrix-core (b >= 3) chain
+# matrix-core (b >= 3) chain.  The table chain's gate+up GEMV leaves one
+# plane of partial sums per K-slice (1024 weights of K at b = 1, 512 at
+# b = 2) for the down GEMV to add up: k = 256 / 128 give one plane, 2176 at
+# b = 1 three (the last slice ragged: 2 of 8 groups), 1024 at b = 2 two,
+# 5120 at b = 2 ten (more planes than the 8 waves that load them).  The
+# matrix-core chain's gate+up GEMV leaves one plane per K-piece (4 groups
+# on these shapes) for the SiLU launch to add up: k = 128 / 256 one, 1024
+# two and 2048 four (one item per work-group), 4096 eight (the persistent
+# kernel: 264 items).
 SMALL = [(128, 128, 1), (256, 384, 2), (384, 256, 3), (512, 640, 5), (1024, 512, 8),
          (256, 1024, 1), (640, 256, 4), (2048, 6144, 2), (256, 8320, 1), (128, 8320, 2),
-         (256, 4224, 3), (128, 4224, 5), (256, 4224, 8)]
+         (2176, 8320, 1), (1024, 8320, 2), (5120, 4224, 2),
+         (256, 4224, 3), (128, 4224, 5), (256, 4224, 8), (1024, 4224, 8), (2048, 4224, 5),
+         (4096, 4224, 3)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
@@ -113,15 +123,17 @@ def test_ffn_small_shapes(fmt, k, f, b):
     _ffn_ok(y.cpu().numpy(), ref, f"ffn {fmt} k={k} f={f} b={b}")
 
 
-@pytest.mark.parametrize("b", [1, 2, 3])
-def test_ffn_zero_gate_gives_exact_zeros(b):
-    """SiLU(0) * up = 0 exactly, through the z paths (formed by the down
-    GEMV itself for b <= 2, by its own launch for b >= 3)."""
+@pytest.mark.parametrize("k,f,b", [(256, 256, 1), (256, 256, 2), (256, 256, 3), (2176, 8320, 1),
+                                   (1024, 8320, 2), (256, 4224, 3), (2048, 4224, 4)])
+def test_ffn_zero_gate_gives_exact_zeros(k, f, b):
+    """SiLU(0) * up = 0 exactly, through every z path: formed by the
+    single-launch down GEMV (f = 256), inside the down table GEMV from the
+    summed planes of partial sums (f = 8320, b <= 2), by its own launch
+    from one or several planes (f = 4224, b >= 3)."""
     import torch
 
-    say(f"ffn zero gate b={b}")
-    g = synth.rng(2100 + b)
-    k, f = 256, 256
+    say(f"ffn zero gate k={k} f={f} b={b}")
+    g = synth.rng(2100 + b + k + f)
     t = synth.ternary(g, (2 * f, k))
     t[:f] = 0
     gu = oracle.t2_pack(t, synth.fp16_uniform(g, (2 * f, k // 128), 0.01, 0.2))
@@ -133,7 +145,8 @@ def test_ffn_zero_gate_gives_exact_zeros(b):
     assert not y.cpu().numpy().any()
 
 
-FULL = [("q1", 5120, 17408, 1), ("q1", 5120, 17408, 5), ("t2", 2048, 6144, 1)]
+FULL = [("q1", 5120, 17408, 1), ("q1", 5120, 17408, 2), ("q1", 5120, 17408, 5),
+        ("t2", 2048, 6144, 1)]
 
 
 @pytest.mark.parametrize("fmt,k,f,b", FULL)

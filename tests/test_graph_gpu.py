@@ -86,8 +86,8 @@ def test_gemv_graph_replays(fmt, n, k, b, path, entry):
 
 
 # (fmt, k, f, b, chain)
-FFN = [("t2", 1024, 4096, 1, "two single-launch GEMVs"), ("q1", 256, 8320, 1, "table chain"),
-       ("q1", 256, 4224, 3, "matrix-core chain")]
+FFN = [("t2", 1024, 4096, 1, "two single-launch GEMVs"), ("q1", 2176, 8320, 1, "table chain"),
+       ("q1", 2048, 4224, 3, "matrix-core chain")]
 
 
 @pytest.mark.parametrize("fmt,k,f,b,chain", FFN)

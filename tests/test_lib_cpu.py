@@ -135,13 +135,17 @@ def test_validation_returns_before_launch(lib):
 def test_ffn_workspace_query_and_validation(lib):
     def a256(v):
         return (v + 255) // 256 * 256
-    # [x prepared for W_gu][h FP32 b x 2f][z prepared for W_dn], 256-aligned
-    # parts; b <= 2 forms z inside the down GEMV and has no z part
+    # [h as P planes FP32 b x 2f][z prepared for W_dn], 256-aligned parts.
+    # P: the gate+up table GEMV's K-slices for b <= 2 (1024 weights of K at
+    # b = 1, 512 at b = 2); for b >= 3 the most K-pieces (at least 4 groups
+    # = 512 weights each) the matrix-core GEMV can take.  b <= 2 forms z
+    # inside the down GEMV and has no z part
     for b in (1, 2, 5, 8):
-        for k, f in ((5120, 17408), (2048, 6144), (128, 128)):
-            want = (a256(lowbit.lowbit_gemv_workspace_bytes("q1", 2 * f, k, b)) + a256(b * 2 * f * 4)
+        for k, f in ((5120, 17408), (2048, 6144), (128, 128), (2176, 8320)):
+            planes = -(-k // (1024 if b == 1 else 512))
+            want = (a256(planes * b * 2 * f * 4)
                     + (a256(lowbit.lowbit_gemv_workspace_bytes("q1", k, f, b)) if b >= 3 else 0))
-            assert lowbit.lowbit_ffn_workspace_bytes("q1", k, f, b) == want
+            assert lowbit.lowbit_ffn_workspace_bytes("q1", k, f, b) == want, (k, f, b)
     assert lowbit.lowbit_ffn_workspace_bytes("q1", 5120, 100, 1) == 0   # f % 128
     assert lowbit.lowbit_ffn_workspace_bytes("q1", 5000, 128, 1) == 0   # k % 128
     assert lowbit.lowbit_ffn_workspace_bytes("q1", 128, 128, 9) == 0
