@@ -101,6 +101,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Output tile of this work-group.  The grid's work-groups go to the CU
+// dies (XCDs, 8 on MI355X, each with its own L2) round-robin by linear
+// index.  When the tile count is a multiple of 8, die x is given the tiles
+// x T/8 .. (x + 1) T/8 - 1 in row-of-tiles order, so that one L2 serves a
+// few whole rows of tiles: every X row of an M tile is then fetched into one
+// L2 instead of into all eight.  (With the N tile fastest, each die had a
+// share of every M tile and streamed all of X through its L2.)
+__device__ __forceinline__ void block_tile(int64_t& tm, int64_t& tn) {
+  const uint32_t nn = gridDim.x, total = gridDim.x * gridDim.y;
+  uint32_t l = blockIdx.x + nn * blockIdx.y;
+  if ((total & 7u) == 0) l = (l & 7u) * (total >> 3) + (l >> 3);
+  tm = l / nn;
+  tn = l % nn;
+}
+
 // Waves with a single 32 x 32 block keep a single LDS buffer per team (three
 // waves per SIMD fit); larger wave blocks double-buffer
 template <int BM, int BN, int WM, int WN>
@@ -148,8 +163,10 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
     return b == 0 ? &xs0[team][0] : &xs1[team][0];
   };
   const int wm = wave / WN, wn = wave % WN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  int64_t tm, tn;
+  block_tile(tm, tn);
+  const int64_t m0 = tm * BM;
+  const int64_t n0 = tn * BN;
   const int64_t groups = k / BK;
   const int64_t chunks = k / kChunk;
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
@@ -654,7 +671,9 @@ __global__ __launch_bounds__(64 * WM * WN * KT, 1) void gemm_team_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, kh = lane >> 5;
 
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  int64_t tm, tn;
+  block_tile(tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int G = (int)(k / BK);
   const int64_t chunks = k / kChunk;
   const int64_t ntiles = (n + kTileRows - 1) / kTileRows;
