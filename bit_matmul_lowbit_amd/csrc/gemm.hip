@@ -103,17 +103,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // Output tile of this work-group.  The grid's work-groups go to the CU
 // dies (XCDs, 8 on MI355X, each with its own L2) round-robin by linear
-// index.  When the tile count is a multiple of 8, die x is given the tiles
-// x T/8 .. (x + 1) T/8 - 1 in row-of-tiles order, so that one L2 serves a
-// few whole rows of tiles: every X row of an M tile is then fetched into one
-// L2 instead of into all eight.  (With the N tile fastest, each die had a
-// share of every M tile and streamed all of X through its L2.)
-__device__ __forceinline__ void block_tile(int64_t& tm, int64_t& tn) {
+// index.  With `xcd` set (the launcher sets it when every tile of the grid
+// runs in the first round of work-groups and the tile count is a multiple
+// of 8), die x is given the tiles x T/8 .. (x + 1) T/8 - 1 in row-of-tiles
+// order, so that one L2 serves a few whole rows of tiles: every X row of
+// an M tile is then fetched into one L2 instead of into all eight (with the
+// N tile fastest, each die held a share of every M tile and streamed all
+// of X through its L2).  Grids of several rounds keep the plain order: the
+// order then also decides which tiles run together, and a 2048x8192x2048
+// 1-bit GEMM ran 14 % slower with the die order.
+__device__ __forceinline__ void block_tile(int xcd, int64_t& tm, int64_t& tn) {
   const uint32_t nn = gridDim.x, total = gridDim.x * gridDim.y;
   uint32_t l = blockIdx.x + nn * blockIdx.y;
-  if ((total & 7u) == 0) l = (l & 7u) * (total >> 3) + (l >> 3);
+  if (xcd) l = (l & 7u) * (total >> 3) + (l >> 3);
   tm = l / nn;
   tn = l % nn;
+}
+
+// the die order applies: one round of work-groups, a multiple of 8 tiles
+inline int xcd_order(dim3 grid) {
+  const int64_t tiles = (int64_t)grid.x * grid.y;
+  return tiles % 8 == 0 && tiles <= (int64_t)device_cu_count() ? 1 : 0;
 }
 
 // Waves with a single 32 x 32 block keep a single LDS buffer per team (three
@@ -126,7 +136,8 @@ constexpr bool kSingleBuffer = BM == 32 * WM && BN == 32 * WN;
 template <int FMT, bool OUT_F32, int BM, int BN, int KT, int WM = 2, int WN = 2>
 __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ? 2 : 1)) void gemm_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y) {
+    const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y,
+    int xcd) {
   constexpr int NT = 64 * WM * WN;                // threads per team
   constexpr int WBM = BM / (32 * WM);             // 32-row blocks per wave
   constexpr int WBN = BN / (32 * WN);             // 32-col blocks per wave
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, (kSingleBuffer<BM, BN, WM, WN> ?
   };
   const int wm = wave / WN, wn = wave % WN;
   int64_t tm, tn;
-  block_tile(tm, tn);
+  block_tile(xcd, tm, tn);
   const int64_t m0 = tm * BM;
   const int64_t n0 = tn * BN;
   const int64_t groups = k / BK;
@@ -643,7 +654,8 @@ __device__ __forceinline__ int sslot(int r, int c) {
 template <int FMT, bool OUT_F32, int BI, int BJ, int WM, int WN, int KT, bool ALL_LIVE>
 __global__ __launch_bounds__(64 * WM * WN * KT, 1) void gemm_team_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y) {
+    const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y,
+    int xcd) {
   constexpr int NWT = WM * WN;        // waves per team
   constexpr int NT = 64 * NWT;        // threads per team
   constexpr int BM = 32 * BI * WM, BN = 32 * BJ * WN;
@@ -672,7 +684,7 @@ __global__ __launch_bounds__(64 * WM * WN * KT, 1) void gemm_team_kernel(
   const int l32 = lane & 31, kh = lane >> 5;
 
   int64_t tm, tn;
-  block_tile(tm, tn);
+  block_tile(xcd, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int G = (int)(k / BK);
   const int64_t chunks = k / kChunk;
@@ -965,11 +977,12 @@ hipError_t launch_team(const uint8_t* codes, const uint16_t* scales, int64_t n, 
   constexpr int BM = 32 * BI * WM, BN = 32 * BJ * WN;
   const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
   const dim3 block(64 * WM * WN * KT);
+  const int xcd = xcd_order(grid);
   // every team has a group at every step when KT divides the group count
   const bool all_live = (k / BK) % KT == 0;
 #define LOWBIT_LAUNCH(OF, AL)                                                                  \
   hipLaunchKernelGGL((gemm_team_kernel<FMT, OF, BI, BJ, WM, WN, KT, AL>), grid, block, 0, st,  \
-                     codes, scales, x, m, n, k, y)
+                     codes, scales, x, m, n, k, y, xcd)
   if (out_f32) {
     if (all_live) LOWBIT_LAUNCH(true, true);
     else LOWBIT_LAUNCH(true, false);
@@ -986,12 +999,13 @@ hipError_t launch_tile(const uint8_t* codes, const uint16_t* scales, int64_t n, 
                        const uint16_t* x, int64_t m, void* y, bool out_f32, hipStream_t st) {
   const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
   const dim3 block(64 * WM * WN * KT);
+  const int xcd = xcd_order(grid);
   if (out_f32)
     hipLaunchKernelGGL((gemm_kernel<FMT, true, BM, BN, KT, WM, WN>), grid, block, 0, st, codes,
-                       scales, x, m, n, k, y);
+                       scales, x, m, n, k, y, xcd);
   else
     hipLaunchKernelGGL((gemm_kernel<FMT, false, BM, BN, KT, WM, WN>), grid, block, 0, st, codes,
-                       scales, x, m, n, k, y);
+                       scales, x, m, n, k, y, xcd);
   return hipGetLastError();
 }
 
