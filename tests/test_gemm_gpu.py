@@ -111,10 +111,14 @@ def test_one_hot_rows_read_weights_exactly(fmt):
 # half-group stages unrolled six at a time -- 2 groups (two stages per
 # team: a tail only), 3 (the second team's last group is past the end), 6
 # (one unrolled pass), 10 (a pass and a four-stage tail); 128 x 128 tiles
-# (2100 x 4100: 561 tiles).
+# (2100 x 4100: 561 tiles).  Grids of one round with a multiple of 8 tiles
+# take their tiles in die order: the 128 x 96 shapes above, and 64 x 64
+# tiles with two K-teams at 500 x 2000 (8 x 32 = 256 tiles, last tile 52
+# rows and 16 columns) and 500 x 500 (64 tiles).
 # Smaller shapes above take 64 x 64 tiles with two K-teams.
 CONFIG_SHAPES = [(600, 2000, 384), (450, 6144, 128), (500, 6100, 256), (500, 6100, 384),
-                 (500, 6100, 768), (512, 6144, 1280), (2100, 4100, 128)]
+                 (500, 6100, 768), (512, 6144, 1280), (2100, 4100, 128), (500, 2000, 384),
+                 (500, 500, 256)]
 
 
 @pytest.mark.parametrize("fmt", ["q1", "t2"])
