@@ -577,10 +577,11 @@ def ceilings():
 
     # the matrix-core GEMV's per-row work (512 weights: byte expansion +
     # one 16x16x32 MFMA) on register data, per SIMD, at one and two waves
-    # per SIMD (the kernel runs two); its floor for the 27B matrices
+    # per SIMD (the kernel runs two); its floor for the 27B matrices, which
+    # the 1-bit persistent kernel runs with the LDS-lookup expansion
     esink = torch.zeros(2 * cus * 256, dtype=torch.float32, device="cuda")
     eres = {}
-    for mode, name in ((0, "expansion+mfma"), (1, "mfma")):
+    for mode, name in ((0, "expansion+mfma"), (1, "mfma"), (2, "lut+mfma")):
         for bpc in (1, 2):
             lowbit.lowbit_probe_expand_mfma(mode, 100, bpc, esink)
             torch.cuda.synchronize()
@@ -592,7 +593,7 @@ def ceilings():
                 torch.cuda.synchronize()
                 ts.append(a.elapsed_time(b) * 1e6 / steps)
             eres[f"{name},{bpc}/simd"] = round(float(np.median(ts)), 2)
-    step_ns = eres["expansion+mfma,2/simd"]
+    step_ns = eres["lut+mfma,2/simd"]
     out["gemv_mfma_row_step"] = {
         "ns_per_row_step_per_simd": eres, "weights_per_row_step": 512,
         "floor_us_at_2_waves_per_simd": {

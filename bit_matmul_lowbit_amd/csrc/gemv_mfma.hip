@@ -261,6 +261,19 @@ __device__ __forceinline__ void lut_pair_mfma(const GroupRegs<1>& r, const uint4
   }
 }
 
+// the table: entry index 8 e + copy, filled by `threads` threads
+__device__ __forceinline__ void lut_fill(uint4* lut, int tid, int threads) {
+  for (int i = tid; i < kLutU4; i += threads) {
+    const uint32_t e = (uint32_t)i / kLutCopies;
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      d[p] = (((e >> (2 * p)) & 1u) ? 0x3C00u : 0xBC00u) |
+             ((((e >> (2 * p + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+    lut[i] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
 __device__ __forceinline__ void group_mfma_lut(const GroupRegs<1>& r, f32x4 (&acc)[16],
                                                const char* tb, uint32_t lb) {
   uint4 t[2][8];
@@ -368,16 +381,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_mfma_kernel(
   const char* tb = reinterpret_cast<const char*>(smem);
   const uint32_t lb = (uint32_t)(lane & (kLutCopies - 1)) << 5;
   if constexpr (FMT == 1) {
-    // the table, while the first loads are in flight: entry index 8 e + copy
-    for (int i = threadIdx.x; i < kLutU4; i += kThreads) {
-      const uint32_t e = (uint32_t)i / kLutCopies;
-      uint32_t d[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        d[p] = (((e >> (2 * p)) & 1u) ? 0x3C00u : 0xBC00u) |
-               ((((e >> (2 * p + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
-      smem[i] = make_uint4(d[0], d[1], d[2], d[3]);
-    }
+    // the table, while the first loads are in flight
+    lut_fill(smem, threadIdx.x, kThreads);
     // LDS only: the loads above stay in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(63));
     stage_barrier();
@@ -575,8 +580,11 @@ __global__ __launch_bounds__(kThreads, FMT == 1 ? 3 : 2) void gemv_mfma_item_ker
 // Ceiling probe (lowbit_probe_expand_mfma): the per-row work of group_mfma
 // -- rep_byte + expand_q1 of one code byte into +-s FP16 operands, and one
 // v_mfma_f32_16x16x32_f16 -- on register data, 16 rows per iteration, the
-// code words changed every iteration.  MODE 0: expansion + MFMA as in the
-// kernel, 1: the MFMA alone on fixed operands.
+// code words changed every iteration.  MODE 0: expansion + MFMA as the
+// ternary and small-matrix kernels run it, 1: the MFMA alone on fixed
+// operands, 2: group_mfma_lut (the 1-bit persistent kernel's lookups, MFMAs
+// and per-group scale FMAs) on register codes, one 128-weight group (64 row
+// steps) per four iterations.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void probe_expand_mfma_kernel(int iters,
                                                                      float* __restrict__ sink) {
@@ -588,7 +596,32 @@ __global__ __launch_bounds__(kThreads) void probe_expand_mfma_kernel(int iters,
   f32x4 acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < iters; ++it) {
+  if constexpr (MODE == 2) {
+    __shared__ uint4 lut[kLutU4];
+    lut_fill(lut, threadIdx.x, kThreads);
+    __syncthreads();
+    GroupRegs<1> r;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      r.c[j] = make_uint4(cw[0] + j, cw[1] ^ j, cw[2] + 3 * j, cw[3] ^ (5 * j));
+      r.x[j] = __builtin_bit_cast(uint4, a);
+    }
+    r.s[0] = make_uint4(ss, ss, ss, ss);
+    r.s[1] = r.s[0];
+    const char* tb = reinterpret_cast<const char*>(lut);
+    const uint32_t lb = (l & (kLutCopies - 1)) << 5;
+    for (int it = 0; it < iters; it += 4) {
+      group_mfma_lut(r, acc, tb, lb);
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) {
+        r.c[j].x += 0x01010101u;
+        r.c[j].y += 0x01010101u;
+        r.c[j].z += 0x01010101u;
+        r.c[j].w += 0x01010101u;
+      }
+    }
+  }
+  for (int it = 0; it < (MODE == 2 ? 0 : iters); ++it) {
 #define LOWBIT_PROBE_ROW(R)                                                                   \
   {                                                                                           \
     const f16x8 bb = MODE == 1 ? a : expand_q1(rep_byte<(R) & 3>(cw[(R) >> 2]), ss);          \
@@ -613,6 +646,8 @@ __global__ __launch_bounds__(kThreads) void probe_expand_mfma_kernel(int iters,
 hipError_t launch_probe_expand_mfma(int mode, int iters, int blocks, float* sink, hipStream_t st) {
   if (mode == 0)
     hipLaunchKernelGGL(probe_expand_mfma_kernel<0>, dim3(blocks), dim3(kThreads), 0, st, iters, sink);
+  else if (mode == 2)
+    hipLaunchKernelGGL(probe_expand_mfma_kernel<2>, dim3(blocks), dim3(kThreads), 0, st, iters, sink);
   else
     hipLaunchKernelGGL(probe_expand_mfma_kernel<1>, dim3(blocks), dim3(kThreads), 0, st, iters, sink);
   return hipGetLastError();

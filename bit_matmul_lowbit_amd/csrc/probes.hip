@@ -145,8 +145,8 @@ int lowbit_probe_mfma_bf16(int iters, int blocks_per_cu, float* sink, hipStream_
 
 int lowbit_probe_expand_mfma(int mode, int iters, int blocks_per_cu, float* sink,
                              hipStream_t stream) {
-  if (!sink || mode < 0 || mode > 1 || blocks_per_cu < 1 || blocks_per_cu > 4 || iters < 1 ||
-      iters > (1 << 24))
+  if (!sink || mode < 0 || mode > 2 || blocks_per_cu < 1 || blocks_per_cu > 4 || iters < 1 ||
+      iters > (1 << 24) || (mode == 2 && iters % 4 != 0))
     return LOWBIT_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(sink) & 3u) return LOWBIT_ERR_ALIGN;
   const int blocks = blocks_per_cu * lowbit::device_cu_count();

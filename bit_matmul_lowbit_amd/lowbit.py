@@ -580,7 +580,8 @@ def lowbit_probe_lds_read(iters: int, blocks_per_cu: int, sink, stream=None):
 
 def lowbit_probe_expand_mfma(mode: int, iters: int, blocks_per_cu: int, sink, stream=None):
     """Probe of the matrix-core GEMV's per-row work (mode 0: expansion +
-    MFMA, 1: the MFMA alone); returns the row steps each SIMD runs."""
+    MFMA, 1: the MFMA alone, 2: LDS-lookup expansion + MFMA + per-group
+    scale, iters a multiple of 4); returns the row steps each SIMD runs."""
     import torch
 
     blocks = blocks_per_cu * lowbit_probe_cu_count()

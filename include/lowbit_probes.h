@@ -62,11 +62,15 @@ int lowbit_probe_lds_read(int iters, int blocks_per_cu, uint32_t* sink, hipStrea
  * weights -- on register data, as the kernel issues them.  Every wave of
  * blocks_per_cu * (compute units) work-groups of 256 threads (so
  * blocks_per_cu waves per SIMD) runs iters x 16 such row steps.  mode 0:
- * expansion + MFMA, 1: the MFMA alone; `sink`
+ * expansion + MFMA, 1: the MFMA alone, 2: the 1-bit persistent kernel's
+ * form -- each code byte an LDS table lookup of eight FP16 values +-1, four
+ * MFMAs per 128-weight group and one FMA by the row's scale per group
+ * (iters a multiple of 4: one group of 64 row steps per 4 iterations); `sink`
  * ([blocks * 256] float, device) is written only if a result equals a
  * fixed constant.  Time / (blocks_per_cu * iters * 16) is the time per row
- * step on one SIMD: with mode 0 and the kernel's two waves per SIMD, the
- * floor that this arithmetic puts under the kernel.  1 <= blocks_per_cu
+ * step on one SIMD: with the kernel's two waves per SIMD, the floor that
+ * this arithmetic puts under the kernel (mode 2 for 1-bit codes on the
+ * persistent kernel, mode 0 otherwise).  1 <= blocks_per_cu
  * <= 4, 1 <= iters <= 2^24.  Returns a lowbit_status. */
 int lowbit_probe_expand_mfma(int mode, int iters, int blocks_per_cu, float* sink,
                              hipStream_t stream);

@@ -269,7 +269,8 @@ def test_probe_header_and_exports(lib):
     assert lib.lowbit_probe_mfma_bf16(100, 9, good, st) == ARG
     assert lib.lowbit_probe_lds_read(100, 5, good, st) == ARG
     assert lib.lowbit_probe_lds_read(0, 2, good, st) == ARG
-    assert lib.lowbit_probe_expand_mfma(2, 100, 2, good, st) == ARG
+    assert lib.lowbit_probe_expand_mfma(3, 100, 2, good, st) == ARG
+    assert lib.lowbit_probe_expand_mfma(2, 101, 2, good, st) == ARG  # mode 2: iters % 4
     assert lib.lowbit_probe_expand_mfma(1, 0, 2, good, st) == ARG
     assert lib.lowbit_probe_expand_mfma(1, 100, 5, good, st) == ARG
     assert lib.lowbit_probe_expand_mfma(1, 100, 2, ctypes.c_void_p(6), st) == ALIGN

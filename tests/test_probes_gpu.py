@@ -33,9 +33,9 @@ def test_probes_run_and_leave_their_sinks():
     assert lowbit.lowbit_probe_mfma_bf16(10, 1, fsink) == cus * 4 * 10 * 4 * 2 * 32 * 32 * 16
     torch.cuda.synchronize()
     assert float(fsink.abs().sum()) == 0.0
-    for mode in (0, 1):
+    for mode in (0, 1, 2):
         say(f"probe expand+mfma mode {mode}")
         fsink = torch.zeros(2 * cus * 256, dtype=torch.float32, device="cuda")
-        assert lowbit.lowbit_probe_expand_mfma(mode, 10, 2, fsink) == 2 * 10 * 16
+        assert lowbit.lowbit_probe_expand_mfma(mode, 12, 2, fsink) == 2 * 12 * 16
         torch.cuda.synchronize()
         assert float(fsink.abs().sum()) == 0.0
