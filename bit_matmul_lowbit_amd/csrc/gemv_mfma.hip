@@ -35,6 +35,9 @@
 // both halves, op_sel), with no byte moves.  A ternary pair also needs the mask of
 // (pos xor neg), so a cell with both bits set is 0, as pos - neg is, and a
 // zero weight contributes an exact 0 (five operations per pair).
+// The 1-bit persistent kernel replaces this expansion with an LDS table
+// lookup of +-1 patterns and applies the scale once per group (see
+// group_mfma_lut below); the item kernel and ternary codes keep it.
 //
 // Work: an item is (16-tile block, K-piece).  The grid is persistent (two
 // work-groups per CU); work-group w takes items w, w + W, ... in order, so
