@@ -33,10 +33,40 @@ namespace {
 // One 16-byte vector of z: 8 consecutive FP16 values of batch row `row`
 // starting at column 8 * chunk, from h = the sum of np planes (FP32
 // [np][b][2f], added in plane order); zeros for a row >= b.
+// With NP > 0 (np = NP planes) the loads of every plane go out before the
+// first add, one round trip in all; NP = 0 takes the planes one at a time.
+template <int NP>
 __device__ __forceinline__ uint4 z_vector(const float* __restrict__ h, int np, int64_t f, int b,
                                           int row, int64_t chunk) {
   if (row >= b) return make_uint4(0u, 0u, 0u, 0u);
   float gv[8], uv[8];
+  if constexpr (NP > 0) {
+    float4 v[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float* hr = h + ((int64_t)p * b + row) * 2 * f;
+      const float4* g4 = reinterpret_cast<const float4*>(hr + chunk * 8);
+      const float4* u4 = reinterpret_cast<const float4*>(hr + f + chunk * 8);
+      v[p][0] = g4[0];
+      v[p][1] = g4[1];
+      v[p][2] = u4[0];
+      v[p][3] = u4[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float gp[8] = {v[p][0].x, v[p][0].y, v[p][0].z, v[p][0].w,
+                           v[p][1].x, v[p][1].y, v[p][1].z, v[p][1].w};
+      const float up[8] = {v[p][2].x, v[p][2].y, v[p][2].z, v[p][2].w,
+                           v[p][3].x, v[p][3].y, v[p][3].z, v[p][3].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        gv[j] = p == 0 ? gp[j] : gv[j] + gp[j];
+        uv[j] = p == 0 ? up[j] : uv[j] + up[j];
+      }
+    }
+    return silu_mul8(gv, uv);
+  }
   for (int p = 0; p < np; ++p) {
     const float* hr = h + ((int64_t)p * b + row) * 2 * f;
     const float4* g4 = reinterpret_cast<const float4*>(hr + chunk * 8);
@@ -59,7 +89,7 @@ __device__ __forceinline__ uint4 z_vector(const float* __restrict__ h, int np, i
 //   MFMA = true:  the matrix-core GEMV's operand order -- vector i = (group
 //                 g, step j, lane l) holds batch row l % 16, chunk
 //                 16 g + 4 j + l / 16, zeros for rows >= b.
-template <bool MFMA>
+template <bool MFMA, int NP = 0>
 __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ h, int np,
                                                        int64_t f, int b, uint4* __restrict__ z,
                                                        int64_t nvec, float* __restrict__ y,
@@ -80,7 +110,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
       row = (int)(i / cpr);
       chunk = i - (int64_t)row * cpr;
     }
-    z[i] = z_vector(h, np, f, b, row, chunk);
+    z[i] = z_vector<NP>(h, np, f, b, row, chunk);
   }
 }
 
@@ -93,10 +123,25 @@ hipError_t launch_silu(const float* h, int64_t np, int64_t f, int64_t b, void* z
   int64_t blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  if (mfma)
-    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, h,
-                       (int)np, f, (int)b, static_cast<uint4*>(z), nvec, y, ycount);
-  else
+  if (mfma) {
+    // the plane count as a template argument up to 8 (the K-pieces of the
+    // gate+up GEMV: 5 at the 27B shape)
+#define LOWBIT_SILU(NPV)                                                                        \
+  hipLaunchKernelGGL((silu_mul_kernel<true, NPV>), dim3((unsigned)blocks), dim3(256), 0, st, h,  \
+                     (int)np, f, (int)b, static_cast<uint4*>(z), nvec, y, ycount)
+    switch (np) {
+      case 1: LOWBIT_SILU(1); break;
+      case 2: LOWBIT_SILU(2); break;
+      case 3: LOWBIT_SILU(3); break;
+      case 4: LOWBIT_SILU(4); break;
+      case 5: LOWBIT_SILU(5); break;
+      case 6: LOWBIT_SILU(6); break;
+      case 7: LOWBIT_SILU(7); break;
+      case 8: LOWBIT_SILU(8); break;
+      default: LOWBIT_SILU(0); break;
+    }
+#undef LOWBIT_SILU
+  } else
     hipLaunchKernelGGL(silu_mul_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, h,
                        (int)np, f, (int)b, static_cast<uint4*>(z), nvec, y, ycount);
   return hipGetLastError();
