@@ -52,6 +52,36 @@ def test_one_hot_reads_single_weight_exactly(fmt, b):
         assert np.array_equal(y, want), (cols, np.abs(y - want).max())
 
 
+# The same on the matrix-core persistent kernel (two-phase API, which always
+# runs the table or matrix-core kernel; 34816 x 1280 at b >= 3 makes 272
+# items, more than the CUs): one product per output, then the group scale
+# applied once (1-bit codes, lookup expansion) or with the operand (ternary),
+# so each output is the weight exactly.
+@pytest.mark.parametrize("fmt", ["q1", "t2"])
+@pytest.mark.parametrize("b", [3, 8])
+def test_one_hot_exact_on_persistent_matrix_core_kernel(fmt, b):
+    import torch
+
+    n, k = 34816, 1280
+    say(f"gemv one-hot persistent {fmt} b={b}")
+    g, codes, scales = _make(fmt, n, k, 700 + b)
+    f = oracle.Q1 if fmt == "q1" else oracle.T2
+    cols = [0, 129, 640, 1279, 511, 512, 3, 1000][:b]
+    dense = oracle.unpack(f, codes, scales, n, k).view(np.float16)[:, cols].astype(np.float64)
+    x = np.zeros((b, k), np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3C00
+    dc, ds, dx = torch.from_numpy(codes).cuda(), dev_u16(scales), dev_u16(x)
+    y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lowbit.lowbit_gemv_workspace_bytes(fmt, n, k, b), dtype=torch.uint8,
+                     device="cuda")
+    lowbit.lowbit_gemv_prepare(n, k, dx, y, ws)
+    lowbit.lowbit_gemv_accumulate(fmt, dc, ds, n, k, b, y, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, dense.T), np.abs(got - dense.T).max()
+
+
 SHAPES = [(1, 128), (16, 128), (37, 384), (300, 1280), (1000, 2176), (129, 4224)]
 
 
